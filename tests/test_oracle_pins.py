@@ -1,0 +1,386 @@
+"""Pins for the CPU oracle: each test checks the oracle against something that
+is fixed independently of it (a brute-force sum, a closed form, a special case
+that reduces to a textbook routine, or a value printed on the pages), chosen
+so that a plausible slip (a dropped term, a wrong sign, a swapped child, the
+wrong tie-break, a leaf locked in too early) fails at least one of them.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+
+def rng_keys(seed, T, d, lo=-4, hi=4):
+    r = np.random.default_rng(seed)
+    return r.integers(lo, hi + 1, size=(T, d)).astype(np.int8)
+
+
+def heap_row(T, level, p):
+    return (T >> level) + p
+
+
+# --------------------------------------------------------------------- O1 ---
+@pytest.mark.parametrize("T,d", [(2, 1), (8, 3), (64, 16), (256, 32), (1024, 5)])
+def test_tree_nodes_equal_prefix_differences(T, d):
+    """Every node equals P[end] - P[start] of brute-force prefix sums."""
+    K = rng_keys(T * 7 + d, T, d, -8, 8)
+    nodes = oracle.build_tree(K)
+    P = np.zeros((T + 1, d), dtype=np.int64)
+    P[1:] = np.cumsum(K.astype(np.int64), axis=0)
+    L = T.bit_length() - 1
+    assert not nodes[0].any(), "row 0 is unused and must stay zero"
+    for level in range(1, L + 1):
+        w = 1 << level
+        for p in range(T >> level):
+            np.testing.assert_array_equal(nodes[heap_row(T, level, p)],
+                                          P[(p + 1) * w] - P[p * w])
+
+
+def test_tree_root_and_levels_sum_to_total():
+    T, d = 512, 24
+    K = rng_keys(5, T, d, -8, 8)
+    nodes = oracle.build_tree(K)
+    total = K.astype(np.int64).sum(axis=0)
+    np.testing.assert_array_equal(nodes[1], total)
+    for level in range(1, 10):
+        rows = nodes[(T >> level):(2 * (T >> level))]
+        np.testing.assert_array_equal(rows.sum(axis=0), total)
+
+
+def cover(m):
+    """Maximal complete subtrees covering [0, m), largest first: (level, start)."""
+    out, a = [], 0
+    for level in range(m.bit_length() - 1, -1, -1):
+        if (m >> level) & 1:
+            out.append((level, a))
+            a += 1 << level
+    return out
+
+
+# --------------------------------------------------------------------- O2 ---
+def test_prefix_matches_cumsum_and_cover_sums():
+    T, d = 256, 8
+    K = rng_keys(11, T, d, -8, 8)
+    S = oracle.prefix(K)
+    np.testing.assert_array_equal(S, np.cumsum(K.astype(np.int64), axis=0))
+    nodes = oracle.build_tree(K)
+    for t in range(T):
+        acc = np.zeros(d, dtype=np.int64)
+        for level, start in cover(t + 1):
+            acc += K[start].astype(np.int64) if level == 0 else nodes[heap_row(T, level, start >> level)]
+        np.testing.assert_array_equal(acc, S[t])
+    np.testing.assert_array_equal(S[T - 1], nodes[1])
+
+
+# --------------------------------------------------------------------- O3 ---
+def test_budget_matches_brute_force_argmax():
+    d, ncls = 16, 32
+    r = np.random.default_rng(3)
+    for trial in range(200):
+        q = r.integers(-9, 10, size=d).astype(np.int8)
+        s = r.integers(-5000, 5000, size=d).astype(np.int64)
+        W = r.integers(-4, 5, size=(ncls, 2 * d)).astype(np.int8)
+        z = W[:, :d].astype(np.int64) @ q.astype(np.int64) + W[:, d:].astype(np.int64) @ s
+        b, logits = oracle.budget(q, s, W)
+        np.testing.assert_array_equal(logits, z)
+        assert b == 3 * (int(np.argmax(z)) + 1)   # np.argmax returns the first maximum
+
+
+def test_budget_ties_go_to_lowest_class_and_caps_hold():
+    d = 8
+    q = np.ones(d, np.int8)
+    s = np.arange(d, dtype=np.int64)
+    W = np.zeros((32, 2 * d), np.int8)
+    assert oracle.budget(q, s, W)[0] == 3           # all logits 0: class 0
+    W[9] = 1
+    W[4] = 1
+    assert oracle.budget(q, s, W)[0] == 15          # classes 4 and 9 tie: class 4
+    W[:] = 0
+    W[31] = 2
+    assert oracle.budget(q, s, W)[0] == 96          # top class: 32 classes x 3 = 96
+    assert oracle.budget(q, s, W, keys_per_class=4)[0] == 96   # 128 capped at 96
+    W[:] = 0
+    W[7, :d] = -1                                   # class 7 only negative: others (0) win
+    assert oracle.budget(q, s, W)[0] == 3
+
+
+# ---------------------------------------------------------------- O4 - O8 ---
+def route_all(K, Q, budgets, window=4, cap=96):
+    nodes = oracle.build_tree(K)
+    out = []
+    for t in range(K.shape[0]):
+        out.append(oracle.route(t, budgets[t], Q[t], K, nodes, window, cap))
+    return out
+
+
+def test_route_invariants_on_uniform_inputs():
+    T, d, w, B = 256, 32, 4, 16
+    K = synth.uniform_i8(1, synth.STREAM_UK, -4, 4, 1, 1, d, 0, T)[0, 0]
+    Q = synth.uniform_i8(1, synth.STREAM_UQ, -4, 4, 1, 1, d, 0, T)[0, 0]
+    for t, (idx, sc, c, st) in enumerate(route_all(K, Q, [B] * T, w)):
+        assert c == min(B, t + 1)
+        sel = idx[:c]
+        assert (idx[c:] == -1).all()
+        assert (np.diff(sel) > 0).all(), "ascending, no duplicates"
+        assert sel[0] >= 0 and sel[-1] == t
+        n = min(w, c)
+        assert set(range(t - n + 1, t + 1)) <= set(sel.tolist())
+        # scores are q . K[j] of the selected keys
+        np.testing.assert_array_equal(sc[:c], K[sel].astype(np.int64) @ Q[t].astype(np.int64))
+        assert st["count"] == c and st["neighbours"] == n
+
+
+def test_route_dense_when_budget_covers_the_prefix():
+    T, d = 64, 8
+    K, Q = rng_keys(1, T, d), rng_keys(2, T, d)
+    for t, (idx, _, c, _) in enumerate(route_all(K, Q, [T] * T, 4, T)):
+        assert c == t + 1
+        np.testing.assert_array_equal(idx[:c], np.arange(t + 1))
+
+
+def test_route_zero_query_ties_pick_lowest_starts():
+    """q = 0 makes every score 0, so the order falls to start position."""
+    T, d, w = 128, 8, 4
+    K = rng_keys(4, T, d)
+    Q = np.zeros((T, d), np.int8)
+    for t, (idx, _, c, _) in enumerate(route_all(K, Q, [20] * T, w)):
+        n = min(w, c)
+        r = c - n
+        expect = list(range(r)) + list(range(t - n + 1, t + 1))
+        np.testing.assert_array_equal(idx[:c], expect)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_route_finds_planted_positive_keys(seed):
+    """r keys with q.k > 0 among zero keys: every node holding one scores > 0,
+    the others 0, so the beam must end on exactly the planted keys."""
+    T, d, w = 256, 16, 4
+    r = np.random.default_rng(100 + seed)
+    t = int(r.integers(40, T))
+    B = int(r.integers(6, 40))
+    n = min(w, B)
+    rr = B - n
+    m = t + 1 - n
+    K = np.zeros((T, d), np.int8)
+    q = r.integers(1, 5, size=d).astype(np.int8)
+    planted = np.sort(r.choice(m, size=rr, replace=False))
+    K[planted] = r.integers(1, 5, size=(rr, d))
+    K[m:] = r.integers(-4, 5, size=(T - m, d))      # neighbours and the future: anything
+    nodes = oracle.build_tree(K)
+    idx, _, c, _ = oracle.route(t, B, q, K, nodes, w)
+    assert c == B
+    np.testing.assert_array_equal(idx[:rr], planted)
+    np.testing.assert_array_equal(idx[rr:c], np.arange(m, t + 1))
+
+
+def test_route_single_negative_key_greedy_path():
+    """r = 1 over one complete subtree [0, 2^h) whose only nonzero key (position
+    0) scores < 0: the left child always loses, ties go left, so the path ends
+    at position 2^(h-1)."""
+    T, d, w = 64, 4, 4
+    for h in range(1, 6):
+        m = 1 << h
+        t = m - 1 + w
+        K = np.zeros((T, d), np.int8)
+        K[0] = -1
+        q = np.ones(d, np.int8)
+        nodes = oracle.build_tree(K)
+        idx, _, c, _ = oracle.route(t, w + 1, q, K, nodes, w)
+        assert c == w + 1
+        assert idx[0] == m // 2
+
+
+def greedy_r1(q, P, m):
+    """Independent greedy argmax-child descent from brute-force prefix sums P."""
+    def sc(start, size):
+        return int((P[start + size] - P[start]).astype(np.int64) @ q.astype(np.int64))
+    roots = [(level, a) for level, a in cover(m)]
+    best = min(roots, key=lambda x: (-sc(x[1], 1 << x[0]), x[1]))
+    level, start = best
+    while level > 0:
+        half = 1 << (level - 1)
+        left, right = sc(start, half), sc(start + half, half)
+        if right > left:
+            start += half
+        level -= 1
+    return start
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_route_width_one_is_greedy_descent(seed):
+    T, d, w = 256, 16, 4
+    K, Q = rng_keys(200 + seed, T, d, -8, 8), rng_keys(300 + seed, T, d, -9, 9)
+    P = np.zeros((T + 1, d), np.int64)
+    P[1:] = np.cumsum(K.astype(np.int64), axis=0)
+    for t, (idx, _, c, st) in enumerate(route_all(K, Q, [w + 1] * T, w)):
+        if c < w + 1:
+            continue
+        m = t + 1 - w
+        assert idx[0] == greedy_r1(Q[t], P, m)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_route_wide_beam_keeps_the_top_leaves(seed):
+    """Domain [0, 2^h) and r >= 2^(h-1): no round before the last drops
+    anything, so the result is the r best single keys (score desc, pos asc)."""
+    T, d, w = 128, 8, 4
+    r = np.random.default_rng(400 + seed)
+    K = r.integers(-2, 3, size=(T, d)).astype(np.int8)   # narrow range: many ties
+    q = r.integers(-2, 3, size=d).astype(np.int8)
+    nodes = oracle.build_tree(K)
+    for h in range(1, 7):
+        m = 1 << h
+        t = m - 1 + w
+        for rr in sorted({max(1, m // 2), (3 * m) // 4, m}):
+            idx, _, c, _ = oracle.route(t, rr + w, q, K, nodes, w, cap=128)
+            s = K[:m].astype(np.int64) @ q.astype(np.int64)
+            order = sorted(range(m), key=lambda j: (-s[j], j))
+            np.testing.assert_array_equal(idx[:rr], np.sort(order[:rr]))
+
+
+def test_route_leaves_stay_and_compete():
+    """Domain [0, 3): cover = {[0,2), [2]}; with r = 2 the leaf 2 must compete
+    with the children of [0,2), i.e. the result is the top two of {0, 1, 2}."""
+    T, d, w = 8, 4, 1
+    r = np.random.default_rng(9)
+    hit_drop = 0
+    for trial in range(300):
+        K = r.integers(-4, 5, size=(T, d)).astype(np.int8)
+        q = r.integers(-4, 5, size=d).astype(np.int8)
+        nodes = oracle.build_tree(K)
+        idx, _, c, _ = oracle.route(3, 3, q, K, nodes, w)
+        s = K[:3].astype(np.int64) @ q.astype(np.int64)
+        top2 = sorted(sorted(range(3), key=lambda j: (-s[j], j))[:2])
+        np.testing.assert_array_equal(idx[:2], top2)
+        hit_drop += 2 not in top2
+    assert hit_drop > 20, "the case where leaf 2 loses must be exercised"
+
+
+def test_route_is_causal():
+    """Changing keys after t (and other queries) leaves query t's route intact."""
+    T, d, w = 128, 8, 4
+    K, Q = rng_keys(21, T, d), rng_keys(22, T, d)
+    base = route_all(K, Q, [24] * T, w)
+    r = np.random.default_rng(5)
+    for t in (0, 5, 37, 64, 100):
+        K2 = K.copy()
+        K2[t + 1:] = r.integers(-4, 5, size=(T - t - 1, d))
+        nodes2 = oracle.build_tree(K2)
+        idx2, sc2, c2, _ = oracle.route(t, 24, Q[t], K2, nodes2, w)
+        np.testing.assert_array_equal(idx2, base[t][0])
+        np.testing.assert_array_equal(sc2, base[t][1])
+
+
+# --------------------------------------------------------------------- O9 ---
+def textbook_causal_attention(Q, K, V, scale):
+    s = (Q.astype(np.float64) @ K.astype(np.float64).T) * scale
+    T = Q.shape[0]
+    s[np.triu_indices(T, 1)] = -np.inf
+    s -= s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ V.astype(np.float64)
+
+
+def test_attention_dense_budget_is_causal_softmax_attention():
+    T, d = 128, 32
+    Q, K = rng_keys(31, T, d), rng_keys(32, T, d)
+    V = synth.values(3, 1, 1, d, 0, T)[0, 0]
+    scale = float(np.float32(1 / np.sqrt(d)))
+    out = oracle.pair_forward(Q, K, V, fixed_budget=T, max_budget=T, scale=scale, cap=T)
+    ref = textbook_causal_attention(Q, K, V, scale)
+    np.testing.assert_allclose(out["O"], ref, rtol=0, atol=1e-6)
+    np.testing.assert_array_equal(out["count"], np.arange(1, T + 1))
+
+
+def test_attention_special_cases():
+    T, d = 64, 16
+    K = rng_keys(41, T, d)
+    V = synth.values(4, 1, 1, d, 0, T)[0, 0]
+    r = np.random.default_rng(2)
+    for _ in range(20):
+        j = r.choice(T, size=int(r.integers(1, 20)), replace=False)
+        q = np.zeros(d, np.int8)
+        # equal logits: the plain mean of the chosen value rows
+        np.testing.assert_allclose(oracle.attend(np.sort(j), q, K, V, 0.25),
+                                   V[j].astype(np.float64).mean(axis=0), atol=1e-6)
+        # one key: exactly its value row
+        q = r.integers(-9, 10, size=d).astype(np.int8)
+        np.testing.assert_array_equal(oracle.attend(j[:1], q, K, V, 0.25), V[j[0]])
+
+
+def test_sparse_attention_equals_masked_dense_attention():
+    torch = pytest.importorskip("torch")
+    T, d = 256, 32
+    Q = synth.uniform_i8(1, synth.STREAM_UQ, -4, 4, 1, 1, d, 0, T)[0, 0]
+    K = synth.uniform_i8(1, synth.STREAM_UK, -4, 4, 1, 1, d, 0, T)[0, 0]
+    V = synth.values(1, 1, 1, d, 0, T)[0, 0]
+    scale = float(np.float32(1 / np.sqrt(d)))
+    out = oracle.pair_forward(Q, K, V, fixed_budget=16, scale=scale)
+    mask = np.zeros((T, T), dtype=bool)
+    for t in range(T):
+        mask[t, out["idx"][t, :out["count"][t]]] = True
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q.astype(np.float64))[None], torch.from_numpy(K.astype(np.float64))[None],
+        torch.from_numpy(V.astype(np.float64))[None], attn_mask=torch.from_numpy(mask)[None],
+        scale=scale)[0].numpy()
+    np.testing.assert_allclose(out["O"], ref, rtol=0, atol=1e-6)
+
+
+# -------------------------------------------------------------------- O10 ---
+def test_decode_append_matches_rebuild_and_prefill_rows():
+    T, d, w = 256, 16, 4
+    seed = 7
+    K = synth.clustered_keys(seed, 1, 1, d, 0, T)[0, 0]
+    Q = synth.copied_queries(seed, 1, 1, d, 0, T)[0, 0]
+    V = synth.values(seed, 1, 1, d, 0, T)[0, 0]
+    W = synth.predictor_weights(seed, 32, d)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    full = oracle.pair_forward(Q, K, V, W=W, scale=scale)
+    n0 = 200
+    Kc = np.zeros_like(K)
+    Kc[:n0] = K[:n0]
+    Vc = np.zeros_like(V)
+    Vc[:n0] = V[:n0]
+    nodes = oracle.build_tree(Kc)
+    pre = K[:n0].astype(np.int64).sum(axis=0)
+    for p in range(n0, T):
+        oracle.append(p, K[p], V[p], Kc, Vc, nodes, pre)
+        b, _ = oracle.budget(Q[p], pre, W)
+        idx, _, c, _ = oracle.route(p, b, Q[p], Kc, nodes, w)
+        o = oracle.attend(idx[:c], Q[p], Kc, Vc, scale)
+        assert b == full["budget"][p] and c == full["count"][p]
+        np.testing.assert_array_equal(idx, full["idx"][p])
+        np.testing.assert_array_equal(o, full["O"][p])
+        if p in (n0, T // 2 + 70, T - 1):
+            Kz = np.zeros_like(K)
+            Kz[:p + 1] = K[:p + 1]
+            np.testing.assert_array_equal(nodes, oracle.build_tree(Kz))
+    np.testing.assert_array_equal(pre, K.astype(np.int64).sum(axis=0))
+
+
+# -------------------------------------------------- value printed on a page --
+def test_dense_mode_keys_per_token_matches_printed_table():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "dense_keys_per_token.txt")
+    rows = {}
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if line:
+            T, printed = line.split()
+            rows[int(T)] = float(printed)
+    assert rows[1024] == 512.5
+    d = 4
+    for T, printed in rows.items():
+        if T == 1024:
+            # run the oracle: a budget of T keys reads every past key
+            K, Q = rng_keys(1, T, d), rng_keys(2, T, d)
+            nodes = oracle.build_tree(K)
+            counts = []
+            for t in range(0, T):
+                counts.append(oracle.route(t, T, Q[t], K, nodes, 4, cap=T)[2])
+            assert np.mean(counts) == printed
+        else:
+            # the page prints the causal mean (T+1)/2 rounded down
+            assert abs((T + 1) / 2 - printed) <= 0.5
