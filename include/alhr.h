@@ -1,0 +1,210 @@
+/*
+ * alhr.h - C ABI of the ALHR tree-attention inference path for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * ALHR (Adaptive Learnable Hierarchical Routing) summarises the keys of each
+ * (batch, head) pair in a static binary tree whose nodes hold the sum of the
+ * key vectors beneath them; a budget predictor maps each query and the
+ * causal key sum to a key budget; the query takes its own and neighbouring
+ * keys, then descends the causal part of the tree along the branches with
+ * the higher q . node_sum score until the budget is filled, and finally runs
+ * softmax attention over only the selected keys.
+ * Sources: the ALHR README ("Adaptive learnable Hierarchical routing:
+ * sub-quadratic tree attention ... (beta)"), sections "Inference stage",
+ * "Training stage" (causality) and "Results and Variables" (caps of 96 keys
+ * and 32 budget classes); decode use from the openai-hub article
+ * "ALHR把注意力变成树搜索", section "ALHR是什么".
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers.  Every array argument is DEVICE memory owned by the caller; the
+ * library never allocates or frees device memory, and keeps no state between
+ * calls.  Scratch space is passed explicitly as (ws, ws_bytes), sized by
+ * alhr_workspace_bytes().  Array base pointers must be 16-byte aligned.
+ * `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ * are asynchronous: results are valid once the caller synchronises `stream`.
+ *
+ * Layouts (row-major, d contiguous; P = batch * heads pairs):
+ *   Q, K   int8  [batch, heads, T, d]     queries / keys
+ *   V, O   fp32  [batch, heads, T, d]     values / attention output
+ *   W      int8  [n_classes, 2d]          predictor weights: columns [0, d)
+ *                                         multiply the query, [d, 2d) the
+ *                                         causal key sum; shared by all pairs
+ *   nodes  int32 [batch, heads, T, d]     tree of key sums in heap order:
+ *          node (level l >= 1, index p), covering keys [p*2^l, (p+1)*2^l),
+ *          is row (T >> l) + p; row 1 is the root; row 0 is never written;
+ *          the children of row i are rows 2i and 2i+1, and a row number
+ *          h >= T stands for key row h - T.
+ *   budget int32 [batch, heads, T]        keys asked for by each query
+ *   idx    int32 [batch, heads, T, max_budget]   selected key positions,
+ *          ascending, padded with -1
+ *   count  int32 [batch, heads, T]        number of selected keys, C_t
+ *
+ * Errors.  Every argument check runs on the host before any launch; a call
+ * that fails a check returns its code and writes nothing.  Launch failures
+ * return ALHR_ERR_DEVICE.  alhr_last_error() gives a thread-local message
+ * for the last non-OK status.  No C++ exception crosses this interface.
+ * Calls on different streams do not share state and may run concurrently.
+ *
+ * Exactness.  Keys and queries are small integers, so node sums, scores and
+ * predictor logits are exact int32 values as long as the declared bounds
+ * hold: the library rejects (ALHR_ERR_OVERFLOW) a configuration for which
+ *   kmax * T                           >= 2^31   (node sums),
+ *   qmax * kmax * d * (T / 2)          >= 2^31   (scores; the root is never
+ *                                                 scored, its halves are),
+ *   wmax * d * (qmax + kmax * T)       >= 2^31   (predictor logits).
+ * The bounds are declared, not measured: data outside them give undefined
+ * (wrong, not unsafe) results.
+ */
+#ifndef ALHR_H
+#define ALHR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum alhr_status {
+    ALHR_OK = 0,
+    ALHR_ERR_ARG = -1,          /* null pointer, bad size or bad parameter   */
+    ALHR_ERR_OVERFLOW = -2,     /* bounds do not guarantee exact int32 sums  */
+    ALHR_ERR_DEVICE = -3,       /* a HIP call or kernel launch failed        */
+    ALHR_ERR_UNSUPPORTED = -4,  /* valid, but not built (e.g. this d)        */
+    ALHR_ERR_WORKSPACE = -5     /* workspace missing or too small            */
+} alhr_status;
+
+typedef struct alhr_config {
+    int32_t batch;           /* B >= 1 (decode: number of sequences)         */
+    int32_t heads;           /* H >= 1; batch * heads <= 65536                */
+    int32_t T;               /* positions = tree capacity: a power of two,
+                                2 <= T <= 2^20                                */
+    int32_t d;               /* head dimension: 16, 32, 64, 128 or 256        */
+    int32_t window;          /* neighbour window w >= 1: key t and the w-1
+                                keys before it                                */
+    int32_t n_classes;       /* budget classes, 1..32                          */
+    int32_t keys_per_class;  /* budget = keys_per_class * (class + 1), >= 1   */
+    int32_t max_budget;      /* cap on the budget and row stride of idx,
+                                1..128                                         */
+    int32_t kmax, qmax, wmax;/* declared bounds on |K|, |Q|, |W| (0..127)     */
+    float scale;             /* softmax scale, normally fl32(1/sqrt(d))       */
+} alhr_config;
+
+/* Bytes of scratch that alhr_predict_budget / alhr_forward need (a multiple
+ * of 256; 0 if cfg is invalid). */
+size_t alhr_workspace_bytes(const alhr_config *cfg);
+
+/* Tree of key sums (README, opening paragraph and "Inference stage": one
+ * static binary tree per layer over the key matrix, each branch keyed by the
+ * sum of the keys beneath it).  Reads K, writes every row 1..T-1 of nodes. */
+alhr_status alhr_build_tree(const alhr_config *cfg, const int8_t *K,
+                            int32_t *nodes, void *stream);
+
+/* Budget predictor (README "Inference stage"; caps in "Results and
+ * Variables"): z_c = W[c][0:d] . Q[t] + W[c][d:2d] . S[t] with the causal
+ * prefix S[t] = sum_{j<=t} K[j]; budget[t] = min(keys_per_class *
+ * (argmax_c z_c + 1), max_budget), ties to the lowest class.  Needs
+ * ws_bytes >= alhr_workspace_bytes(cfg). */
+alhr_status alhr_predict_budget(const alhr_config *cfg, const int8_t *Q,
+                                const int8_t *K, const int8_t *W,
+                                int32_t *budget, void *ws, size_t ws_bytes,
+                                void *stream);
+
+/* Routing (README "Inference stage" and "Training stage"): for each query t
+ * with budget B_t (budget[t], or fixed_budget when budget is NULL; values
+ * must lie in [1, max_budget]): C_t = min(B_t, t+1) keys; the n_t =
+ * min(window, C_t) keys t, t-1, ...; then a beam of width r_t = C_t - n_t
+ * descends from the maximal complete subtrees covering [0, t+1-n_t),
+ * expanding every internal beam node each round and keeping the r_t best
+ * nodes by (q . node_sum descending, first position ascending).  Writes idx
+ * and count. */
+alhr_status alhr_route(const alhr_config *cfg, const int8_t *Q,
+                       const int8_t *K, const int32_t *nodes,
+                       const int32_t *budget, int32_t fixed_budget,
+                       int32_t *idx, int32_t *count, void *stream);
+
+/* Per-query load counts of the routing step, for byte accounting: stats is
+ * int32 [batch, heads, T, 4] = (tree rows loaded, key rows loaded in the
+ * descent, neighbour key rows, selected keys).  Same arguments as
+ * alhr_route; idx and count are written as by alhr_route. */
+alhr_status alhr_route_stats(const alhr_config *cfg, const int8_t *Q,
+                             const int8_t *K, const int32_t *nodes,
+                             const int32_t *budget, int32_t fixed_budget,
+                             int32_t *idx, int32_t *count, int32_t *stats,
+                             void *stream);
+
+/* Sparse attention over selected keys (README "Inference stage"): for each
+ * query, a_j = scale * (Q[t] . K[j]) over j in idx[t][0..count[t]), and
+ * O[t] = sum_j softmax(a)_j V[j], in fp32. */
+alhr_status alhr_sparse_attend(const alhr_config *cfg, const int8_t *Q,
+                               const int8_t *K, const float *V,
+                               const int32_t *idx, const int32_t *count,
+                               float *O, void *stream);
+
+/* Fused routing + attention in one pass per query (same results as
+ * alhr_route followed by alhr_sparse_attend; the leaf scores found by the
+ * descent are reused as logits). */
+alhr_status alhr_route_attend(const alhr_config *cfg, const int8_t *Q,
+                              const int8_t *K, const float *V,
+                              const int32_t *nodes, const int32_t *budget,
+                              int32_t fixed_budget, int32_t *idx,
+                              int32_t *count, float *O, void *stream);
+
+/* The whole prefill path: build the tree, predict budgets (W != NULL; else
+ * every query uses fixed_budget), route and attend.  budget (nullable)
+ * receives the predicted budgets.  ws as for alhr_predict_budget (unused
+ * when W is NULL). */
+alhr_status alhr_forward(const alhr_config *cfg, const int8_t *Q,
+                         const int8_t *K, const float *V, const int8_t *W,
+                         int32_t fixed_budget, int32_t *nodes,
+                         int32_t *budget, int32_t *idx, int32_t *count,
+                         float *O, void *ws, size_t ws_bytes, void *stream);
+
+/* Decode cache set-up: prefix[b, h] = sum_{j < n} K[j] (int32 [batch, heads,
+ * d]) read from the tree as the sum of the maximal complete subtrees
+ * covering [0, n); 0 <= n <= T (n = 0 gives zeros). */
+alhr_status alhr_prefix_from_tree(const alhr_config *cfg, int32_t n,
+                                  const int8_t *K, const int32_t *nodes,
+                                  int32_t *prefix, void *stream);
+
+/* Decode append at position pos, the same for every pair (openai-hub
+ * article, "ALHR是什么": one new token at a time): K[pos] = k_new,
+ * V[pos] = v_new, nodes(l, pos >> l) += k_new for every level l >= 1, and
+ * prefix += k_new (so prefix holds S[pos] afterwards).  k_new int8 and v_new
+ * fp32 are [batch, heads, d].  Precondition: key rows >= pos are zero and
+ * nodes is the tree of those keys (rebuilding after appends gives the same
+ * table). */
+alhr_status alhr_append(const alhr_config *cfg, int32_t pos,
+                        const int8_t *k_new, const float *v_new, int8_t *K,
+                        float *V, int32_t *nodes, int32_t *prefix,
+                        void *stream);
+
+/* Decode step: route and attend the single query q_new (int8 [batch, heads,
+ * d]) at position pos of every pair, after alhr_append(pos).  The budget
+ * comes from W and prefix (= S[pos]) when W != NULL, else fixed_budget.
+ * Outputs are per pair: budget (nullable) int32 [batch, heads], idx int32
+ * [batch, heads, max_budget], count int32 [batch, heads], O fp32 [batch,
+ * heads, d]. */
+alhr_status alhr_decode_step(const alhr_config *cfg, int32_t pos,
+                             const int8_t *q_new, const int8_t *K,
+                             const float *V, const int32_t *nodes,
+                             const int32_t *prefix, const int8_t *W,
+                             int32_t fixed_budget, int32_t *budget,
+                             int32_t *idx, int32_t *count, float *O,
+                             void *stream);
+
+/* Static text for a status code. */
+const char *alhr_status_string(alhr_status status);
+
+/* Thread-local detail of the last non-OK status on this thread ("" if none). */
+const char *alhr_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t alhr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ALHR_H */

@@ -1,0 +1,82 @@
+"""Build the gfx950 shared libraries in-tree with hipcc.
+
+    python -m learned_tree_routed_amd.build
+
+builds ``learned_tree_routed_amd/libalhr.so`` (the C ABI of include/alhr.h)
+and ``synth/libalhr_synth.so`` (the device-side input generator).  Every HIP
+source is compiled for gfx950 only, with packed-FP32 instruction selection
+turned off.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libalhr.so")
+SYNTH_DIR = os.path.join(ROOT, "synth")
+SYNTH_LIB = os.path.join(SYNTH_DIR, "libalhr_synth.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I" + os.path.join(ROOT, "include"),
+]
+
+SOURCES = ["api.hip", "build.hip", "predict.hip", "route.hip", "decode.hip"]
+
+
+def _run(cmd):
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature and says so; harmless
+    out = "\n".join(l for l in p.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if p.returncode != 0:
+        raise RuntimeError("command failed (%d): %s\n%s" % (p.returncode, " ".join(cmd), out))
+    return out
+
+
+def _compile(src, obj):
+    return _run([HIPCC] + FLAGS + ["-c", src, "-o", obj])
+
+
+def _link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
+    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
+    os.replace(tmp, out)
+
+
+def build_alhr(jobs=8):
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(_compile, [os.path.join(CSRC, s) for s in SOURCES], objs))
+    _link(objs, LIB)
+    return LIB
+
+
+def build_synth():
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    obj = os.path.join(BUILD_DIR, "synth_device.o")
+    _compile(os.path.join(SYNTH_DIR, "synth_device.hip"), obj)
+    _link([obj], SYNTH_LIB)
+    return SYNTH_LIB
+
+
+def build_all(jobs=8):
+    with cf.ThreadPoolExecutor(max_workers=2) as ex:
+        a = ex.submit(build_alhr, jobs)
+        b = ex.submit(build_synth)
+        return a.result(), b.result()
+
+
+if __name__ == "__main__":
+    for p in build_all():
+        print("built", p)
+    sys.exit(0)

@@ -1,0 +1,351 @@
+// C ABI of libalhr: argument validation on the host, then kernel launches on
+// the caller's stream.  Every check runs before the first HIP call, so a
+// rejected call touches neither the device nor the outputs.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/alhr.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+alhr_status fail(alhr_status st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+alhr_status ok()
+{
+    g_last_error.clear();
+    return ALHR_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define ALHR_NEED_PTR(p)                                                                  \
+    do {                                                                                  \
+        if (!(p)) return fail(ALHR_ERR_ARG, "%s: argument '%s' is NULL", fn, #p);         \
+        if (!aligned16(p))                                                                \
+            return fail(ALHR_ERR_ARG, "%s: argument '%s' is not 16-byte aligned", fn, #p); \
+    } while (0)
+
+alhr_status check_config(const char* fn, const alhr_config* c, alhr::Shape* s)
+{
+    if (!c) return fail(ALHR_ERR_ARG, "%s: cfg is NULL", fn);
+    if (c->batch < 1 || c->heads < 1)
+        return fail(ALHR_ERR_ARG, "%s: batch (%d) and heads (%d) must be >= 1", fn, c->batch,
+                    c->heads);
+    if ((int64_t)c->batch * c->heads > 65536)
+        return fail(ALHR_ERR_ARG, "%s: batch * heads = %lld exceeds 65536", fn,
+                    (long long)c->batch * c->heads);
+    if (c->T < 2 || c->T > (1 << 20) || (c->T & (c->T - 1)))
+        return fail(ALHR_ERR_ARG, "%s: T = %d must be a power of two in [2, 2^20]", fn, c->T);
+    if (c->d < 1 || c->d % 16)
+        return fail(ALHR_ERR_ARG, "%s: d = %d must be a positive multiple of 16", fn, c->d);
+    if (c->d != 16 && c->d != 32 && c->d != 64 && c->d != 128 && c->d != 256)
+        return fail(ALHR_ERR_UNSUPPORTED, "%s: d = %d is not built (16, 32, 64, 128, 256)", fn,
+                    c->d);
+    if (c->window < 1) return fail(ALHR_ERR_ARG, "%s: window = %d must be >= 1", fn, c->window);
+    if (c->n_classes < 1 || c->n_classes > 32)
+        return fail(ALHR_ERR_ARG, "%s: n_classes = %d must be in [1, 32]", fn, c->n_classes);
+    if (c->keys_per_class < 1)
+        return fail(ALHR_ERR_ARG, "%s: keys_per_class = %d must be >= 1", fn,
+                    c->keys_per_class);
+    if (c->max_budget < 1 || c->max_budget > 128)
+        return fail(ALHR_ERR_ARG, "%s: max_budget = %d must be in [1, 128]", fn, c->max_budget);
+    if (c->kmax < 0 || c->kmax > 127 || c->qmax < 0 || c->qmax > 127 || c->wmax < 0 ||
+        c->wmax > 127)
+        return fail(ALHR_ERR_ARG, "%s: kmax, qmax, wmax must be in [0, 127]", fn);
+    if (!std::isfinite(c->scale)) return fail(ALHR_ERR_ARG, "%s: scale is not finite", fn);
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t T = c->T, d = c->d;
+    if ((int64_t)c->kmax * T >= lim)
+        return fail(ALHR_ERR_OVERFLOW, "%s: kmax * T = %lld reaches 2^31 (node sums)", fn,
+                    (long long)(c->kmax * T));
+    if ((int64_t)c->qmax * c->kmax * d * (T / 2) >= lim)
+        return fail(ALHR_ERR_OVERFLOW, "%s: qmax * kmax * d * T/2 = %lld reaches 2^31 (scores)",
+                    fn, (long long)((int64_t)c->qmax * c->kmax * d * (T / 2)));
+    if ((int64_t)c->wmax * d * (c->qmax + (int64_t)c->kmax * T) >= lim)
+        return fail(ALHR_ERR_OVERFLOW, "%s: wmax * d * (qmax + kmax * T) reaches 2^31 (logits)",
+                    fn);
+    if (s) {
+        s->P = c->batch * c->heads;
+        s->T = c->T;
+        int L = 0;
+        while ((1 << L) < c->T) ++L;
+        s->L = L;
+        s->d = c->d;
+        s->window = c->window;
+        s->n_classes = c->n_classes;
+        s->keys_per_class = c->keys_per_class;
+        s->max_budget = c->max_budget;
+        s->scale = c->scale;
+        // every scored node has at most T/2 keys: its entries fit 24 signed bits?
+        s->mul24 = (int64_t)c->kmax * (T / 2) < ((int64_t)1 << 23);
+    }
+    return ALHR_OK;
+}
+
+alhr_status check_fixed(const char* fn, const alhr_config* c, const int32_t* budget, int32_t fb)
+{
+    if (!budget && (fb < 1 || fb > c->max_budget))
+        return fail(ALHR_ERR_ARG, "%s: fixed_budget = %d must be in [1, max_budget = %d]", fn,
+                    fb, c->max_budget);
+    if (budget && !aligned16(budget))
+        return fail(ALHR_ERR_ARG, "%s: argument 'budget' is not 16-byte aligned", fn);
+    return ALHR_OK;
+}
+
+alhr_status device_status(const char* fn, hipError_t e)
+{
+    if (e != hipSuccess)
+        return fail(ALHR_ERR_DEVICE, "%s: %s (%s)", fn, hipGetErrorName(e), hipGetErrorString(e));
+    return ok();
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t alhr_version(void) { return 100; }
+
+const char* alhr_status_string(alhr_status s)
+{
+    switch (s) {
+        case ALHR_OK: return "ALHR_OK";
+        case ALHR_ERR_ARG: return "ALHR_ERR_ARG: invalid argument";
+        case ALHR_ERR_OVERFLOW: return "ALHR_ERR_OVERFLOW: declared bounds overflow int32";
+        case ALHR_ERR_DEVICE: return "ALHR_ERR_DEVICE: HIP runtime or launch failure";
+        case ALHR_ERR_UNSUPPORTED: return "ALHR_ERR_UNSUPPORTED: configuration not built";
+        case ALHR_ERR_WORKSPACE: return "ALHR_ERR_WORKSPACE: workspace missing or too small";
+    }
+    return "unknown alhr_status";
+}
+
+const char* alhr_last_error(void) { return g_last_error.c_str(); }
+
+size_t alhr_workspace_bytes(const alhr_config* cfg)
+{
+    alhr::Shape s;
+    if (check_config("alhr_workspace_bytes", cfg, &s) != ALHR_OK) return 0;
+    return alhr::predict_ws_bytes(s);
+}
+
+alhr_status alhr_build_tree(const alhr_config* cfg, const int8_t* K, int32_t* nodes,
+                            void* stream)
+{
+    const char* fn = "alhr_build_tree";
+    alhr::Shape s;
+    if (alhr_status st = check_config(fn, cfg, &s)) return st;
+    ALHR_NEED_PTR(K);
+    ALHR_NEED_PTR(nodes);
+    (void)hipGetLastError();
+    return device_status(fn, alhr::launch_build(s, K, nodes, as_stream(stream)));
+}
+
+alhr_status alhr_predict_budget(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
+                                const int8_t* W, int32_t* budget, void* ws, size_t ws_bytes,
+                                void* stream)
+{
+    const char* fn = "alhr_predict_budget";
+    alhr::Shape s;
+    if (alhr_status st = check_config(fn, cfg, &s)) return st;
+    ALHR_NEED_PTR(Q);
+    ALHR_NEED_PTR(K);
+    ALHR_NEED_PTR(W);
+    ALHR_NEED_PTR(budget);
+    const size_t need = alhr::predict_ws_bytes(s);
+    if (!ws || ws_bytes < need || !aligned16(ws))
+        return fail(ALHR_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu%s)", fn, need,
+                    ws_bytes, ws ? "" : ", NULL");
+    (void)hipGetLastError();
+    return device_status(fn, alhr::launch_predict(s, Q, K, W, budget, ws, as_stream(stream)));
+}
+
+static alhr_status route_common(const char* fn, const alhr_config* cfg, const int8_t* Q,
+                                const int8_t* K, const float* V, const int32_t* nodes,
+                                const int32_t* budget, int32_t fixed_budget, int32_t* idx,
+                                int32_t* count, float* O, int32_t* stats, bool attend,
+                                void* stream)
+{
+    alhr::Shape s;
+    if (alhr_status st = check_config(fn, cfg, &s)) return st;
+    ALHR_NEED_PTR(Q);
+    ALHR_NEED_PTR(K);
+    ALHR_NEED_PTR(nodes);
+    ALHR_NEED_PTR(idx);
+    ALHR_NEED_PTR(count);
+    if (attend) {
+        ALHR_NEED_PTR(V);
+        ALHR_NEED_PTR(O);
+    }
+    if (alhr_status st = check_fixed(fn, cfg, budget, fixed_budget)) return st;
+    (void)hipGetLastError();
+    return device_status(fn, alhr::launch_route(s, Q, K, attend ? V : nullptr, nodes, budget,
+                                                fixed_budget, idx, count, attend ? O : nullptr,
+                                                stats, as_stream(stream)));
+}
+
+alhr_status alhr_route(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
+                       const int32_t* nodes, const int32_t* budget, int32_t fixed_budget,
+                       int32_t* idx, int32_t* count, void* stream)
+{
+    return route_common("alhr_route", cfg, Q, K, nullptr, nodes, budget, fixed_budget, idx,
+                        count, nullptr, nullptr, false, stream);
+}
+
+alhr_status alhr_route_stats(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
+                             const int32_t* nodes, const int32_t* budget, int32_t fixed_budget,
+                             int32_t* idx, int32_t* count, int32_t* stats, void* stream)
+{
+    const char* fn = "alhr_route_stats";
+    ALHR_NEED_PTR(stats);
+    return route_common(fn, cfg, Q, K, nullptr, nodes, budget, fixed_budget, idx, count,
+                        nullptr, stats, false, stream);
+}
+
+alhr_status alhr_sparse_attend(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
+                               const float* V, const int32_t* idx, const int32_t* count,
+                               float* O, void* stream)
+{
+    const char* fn = "alhr_sparse_attend";
+    alhr::Shape s;
+    if (alhr_status st = check_config(fn, cfg, &s)) return st;
+    ALHR_NEED_PTR(Q);
+    ALHR_NEED_PTR(K);
+    ALHR_NEED_PTR(V);
+    ALHR_NEED_PTR(idx);
+    ALHR_NEED_PTR(count);
+    ALHR_NEED_PTR(O);
+    (void)hipGetLastError();
+    return device_status(fn, alhr::launch_attend(s, Q, K, V, idx, count, O, as_stream(stream)));
+}
+
+alhr_status alhr_route_attend(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
+                              const float* V, const int32_t* nodes, const int32_t* budget,
+                              int32_t fixed_budget, int32_t* idx, int32_t* count, float* O,
+                              void* stream)
+{
+    return route_common("alhr_route_attend", cfg, Q, K, V, nodes, budget, fixed_budget, idx,
+                        count, O, nullptr, true, stream);
+}
+
+alhr_status alhr_forward(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
+                         const float* V, const int8_t* W, int32_t fixed_budget, int32_t* nodes,
+                         int32_t* budget, int32_t* idx, int32_t* count, float* O, void* ws,
+                         size_t ws_bytes, void* stream)
+{
+    const char* fn = "alhr_forward";
+    alhr::Shape s;
+    if (alhr_status st = check_config(fn, cfg, &s)) return st;
+    ALHR_NEED_PTR(Q);
+    ALHR_NEED_PTR(K);
+    ALHR_NEED_PTR(V);
+    ALHR_NEED_PTR(nodes);
+    ALHR_NEED_PTR(idx);
+    ALHR_NEED_PTR(count);
+    ALHR_NEED_PTR(O);
+    if (W) {
+        if (!aligned16(W)) return fail(ALHR_ERR_ARG, "%s: argument 'W' is not 16-byte aligned", fn);
+        if (!budget)
+            return fail(ALHR_ERR_ARG, "%s: 'budget' must be given when W is (it holds the "
+                                      "predicted budgets)", fn);
+        if (!aligned16(budget))
+            return fail(ALHR_ERR_ARG, "%s: argument 'budget' is not 16-byte aligned", fn);
+        const size_t need = alhr::predict_ws_bytes(s);
+        if (!ws || ws_bytes < need || !aligned16(ws))
+            return fail(ALHR_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu%s)", fn,
+                        need, ws_bytes, ws ? "" : ", NULL");
+    } else if (fixed_budget < 1 || fixed_budget > cfg->max_budget) {
+        return fail(ALHR_ERR_ARG, "%s: fixed_budget = %d must be in [1, max_budget = %d]", fn,
+                    fixed_budget, cfg->max_budget);
+    }
+    hipStream_t st = as_stream(stream);
+    (void)hipGetLastError();
+    hipError_t e = alhr::launch_build(s, K, nodes, st);
+    if (e == hipSuccess && W) e = alhr::launch_predict(s, Q, K, W, budget, ws, st);
+    if (e == hipSuccess)
+        e = alhr::launch_route(s, Q, K, V, nodes, W ? budget : nullptr, fixed_budget, idx, count,
+                               O, nullptr, st);
+    return device_status(fn, e);
+}
+
+alhr_status alhr_prefix_from_tree(const alhr_config* cfg, int32_t n, const int8_t* K,
+                                  const int32_t* nodes, int32_t* prefix, void* stream)
+{
+    const char* fn = "alhr_prefix_from_tree";
+    alhr::Shape s;
+    if (alhr_status st = check_config(fn, cfg, &s)) return st;
+    if (n < 0 || n > cfg->T) return fail(ALHR_ERR_ARG, "%s: n = %d must be in [0, T]", fn, n);
+    ALHR_NEED_PTR(K);
+    ALHR_NEED_PTR(nodes);
+    ALHR_NEED_PTR(prefix);
+    (void)hipGetLastError();
+    return device_status(fn, alhr::launch_prefix_from_tree(s, n, K, nodes, prefix,
+                                                           as_stream(stream)));
+}
+
+alhr_status alhr_append(const alhr_config* cfg, int32_t pos, const int8_t* k_new,
+                        const float* v_new, int8_t* K, float* V, int32_t* nodes, int32_t* prefix,
+                        void* stream)
+{
+    const char* fn = "alhr_append";
+    alhr::Shape s;
+    if (alhr_status st = check_config(fn, cfg, &s)) return st;
+    if (pos < 0 || pos >= cfg->T) return fail(ALHR_ERR_ARG, "%s: pos = %d outside [0, T)", fn, pos);
+    ALHR_NEED_PTR(k_new);
+    ALHR_NEED_PTR(v_new);
+    ALHR_NEED_PTR(K);
+    ALHR_NEED_PTR(V);
+    ALHR_NEED_PTR(nodes);
+    ALHR_NEED_PTR(prefix);
+    (void)hipGetLastError();
+    return device_status(fn, alhr::launch_append(s, pos, k_new, v_new, K, V, nodes, prefix,
+                                                 as_stream(stream)));
+}
+
+alhr_status alhr_decode_step(const alhr_config* cfg, int32_t pos, const int8_t* q_new,
+                             const int8_t* K, const float* V, const int32_t* nodes,
+                             const int32_t* prefix, const int8_t* W, int32_t fixed_budget,
+                             int32_t* budget, int32_t* idx, int32_t* count, float* O,
+                             void* stream)
+{
+    const char* fn = "alhr_decode_step";
+    alhr::Shape s;
+    if (alhr_status st = check_config(fn, cfg, &s)) return st;
+    if (pos < 0 || pos >= cfg->T) return fail(ALHR_ERR_ARG, "%s: pos = %d outside [0, T)", fn, pos);
+    ALHR_NEED_PTR(q_new);
+    ALHR_NEED_PTR(K);
+    ALHR_NEED_PTR(V);
+    ALHR_NEED_PTR(nodes);
+    ALHR_NEED_PTR(idx);
+    ALHR_NEED_PTR(count);
+    ALHR_NEED_PTR(O);
+    if (W) {
+        ALHR_NEED_PTR(prefix);
+        if (!aligned16(W)) return fail(ALHR_ERR_ARG, "%s: argument 'W' is not 16-byte aligned", fn);
+    } else if (fixed_budget < 1 || fixed_budget > cfg->max_budget) {
+        return fail(ALHR_ERR_ARG, "%s: fixed_budget = %d must be in [1, max_budget = %d]", fn,
+                    fixed_budget, cfg->max_budget);
+    }
+    if (budget && !aligned16(budget))
+        return fail(ALHR_ERR_ARG, "%s: argument 'budget' is not 16-byte aligned", fn);
+    (void)hipGetLastError();
+    return device_status(fn, alhr::launch_decode(s, pos, q_new, K, V, nodes, prefix, W,
+                                                 fixed_budget, budget, idx, count, O,
+                                                 as_stream(stream)));
+}
+
+}  // extern "C"

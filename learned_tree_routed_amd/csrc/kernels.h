@@ -1,0 +1,50 @@
+// Internal launch interface between the C ABI layer and the gfx950 kernels.
+// Every launcher assumes its arguments were validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace alhr {
+
+struct Shape {
+    int P;            // batch * heads pairs
+    int T;            // positions per pair (power of two)
+    int L;            // log2(T)
+    int d;            // head dimension
+    int window;
+    int n_classes;
+    int keys_per_class;
+    int max_budget;
+    float scale;
+    bool mul24;       // every scored tree node fits a signed 24-bit multiply
+};
+
+// Scratch for the predictor: one int32 per (pair, chunk, class).
+size_t predict_ws_bytes(const Shape& s);
+
+hipError_t launch_build(const Shape& s, const int8_t* K, int32_t* nodes, hipStream_t st);
+
+hipError_t launch_predict(const Shape& s, const int8_t* Q, const int8_t* K, const int8_t* W,
+                          int32_t* budget, void* ws, hipStream_t st);
+
+// O == nullptr: routing only; stats != nullptr: also write per-query load counts.
+hipError_t launch_route(const Shape& s, const int8_t* Q, const int8_t* K, const float* V,
+                        const int32_t* nodes, const int32_t* budget, int fixed_budget,
+                        int32_t* idx, int32_t* count, float* O, int32_t* stats, hipStream_t st);
+
+hipError_t launch_attend(const Shape& s, const int8_t* Q, const int8_t* K, const float* V,
+                         const int32_t* idx, const int32_t* count, float* O, hipStream_t st);
+
+hipError_t launch_prefix_from_tree(const Shape& s, int n, const int8_t* K, const int32_t* nodes,
+                                   int32_t* prefix, hipStream_t st);
+
+hipError_t launch_append(const Shape& s, int pos, const int8_t* k_new, const float* v_new,
+                         int8_t* K, float* V, int32_t* nodes, int32_t* prefix, hipStream_t st);
+
+hipError_t launch_decode(const Shape& s, int pos, const int8_t* q_new, const int8_t* K,
+                         const float* V, const int32_t* nodes, const int32_t* prefix,
+                         const int8_t* W, int fixed_budget, int32_t* budget, int32_t* idx,
+                         int32_t* count, float* O, hipStream_t st);
+
+}  // namespace alhr

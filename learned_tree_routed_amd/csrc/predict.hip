@@ -1,0 +1,198 @@
+// Budget predictor (ALHR README "Inference stage"; caps in "Results and
+// Variables"): z_c(t) = W[c][0:d] . Q[t] + W[c][d:2d] . S[t] with the causal
+// key sum S[t] = sum_{j<=t} K[j]; budget = min(kpc * (first argmax + 1), cap).
+//
+// S[t] is never formed.  Because the map is linear, W_s . S[t] is the
+// inclusive scan over j <= t of u[j][c] = W_s[c] . K[j], which is exact in
+// int32 under the declared bounds.  Two launches per call:
+//   1. per chunk of 256 positions, the chunk totals of u (int32 workspace);
+//   2. per chunk, the offsets from earlier chunks, an in-LDS scan of u over
+//      the chunk, the query term W_q . Q[t] and the argmax.
+// The dot products use the packed int8 dot instruction (4 MACs per op); at
+// 2 * d MACs per class and query this is far too small to pay for MFMA.
+#include "device.h"
+#include "kernels.h"
+
+namespace alhr {
+namespace {
+
+constexpr int kChunk = 256;        // positions per workgroup (one per thread)
+constexpr int kMaxClasses = 32;
+
+__host__ __device__ inline size_t chunks_per_pair(int T) { return (size_t)((T + kChunk - 1) / kChunk); }
+
+// u[c] = W_s[c] . k for every class; W staged in LDS as words.
+template <int D>
+__device__ __forceinline__ void class_dots(const int* __restrict__ kw, const int* __restrict__ wl,
+                                           int nc, int col0, int (&u)[kMaxClasses])
+{
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) {
+        int acc = 0;
+        if (c < nc) {
+            const int* w = wl + c * (D / 2) + col0;
+#pragma unroll
+            for (int i = 0; i < D / 4; ++i) acc = dot4_i8(kw[i], w[i], acc);
+        }
+        u[c] = acc;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void stage_weights(const int8_t* __restrict__ W, int nc, int* wl)
+{
+    const int* w = reinterpret_cast<const int*>(W);
+    for (int i = threadIdx.x; i < nc * (D / 2); i += kChunk) wl[i] = w[i];
+}
+
+template <int D>
+__global__ __launch_bounds__(kChunk) void k_predict_chunks(const int8_t* __restrict__ K,
+                                                           const int8_t* __restrict__ W,
+                                                           int32_t* __restrict__ tot, int T, int nc)
+{
+    __shared__ int wl[kMaxClasses * D / 2];
+    __shared__ int part[kChunk / 32][kMaxClasses + 1];
+    __shared__ int us[kChunk][kMaxClasses + 1];
+    const int nch = (int)chunks_per_pair(T);
+    const int pair = blockIdx.x / nch, chunk = blockIdx.x % nch;
+    stage_weights<D>(W, nc, wl);
+    __syncthreads();
+    const int t = chunk * kChunk + threadIdx.x;
+    int u[kMaxClasses];
+    if (t < T) {
+        int kw[D / 4];
+        const int* kr = reinterpret_cast<const int*>(K + ((size_t)pair * T + t) * D);
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) kw[i] = kr[i];
+        class_dots<D>(kw, wl, nc, D / 4, u);
+    } else {
+#pragma unroll
+        for (int c = 0; c < kMaxClasses; ++c) u[c] = 0;
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) us[threadIdx.x][c] = u[c];
+    __syncthreads();
+    {   // thread (segment, class) sums 32 positions
+        const int c = threadIdx.x % kMaxClasses, seg = threadIdx.x / kMaxClasses;
+        int acc = 0;
+        for (int j = 0; j < 32; ++j) acc += us[seg * 32 + j][c];
+        part[seg][c] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x < nc) {
+        int acc = 0;
+        for (int seg = 0; seg < kChunk / 32; ++seg) acc += part[seg][threadIdx.x];
+        tot[((size_t)pair * nch + chunk) * kMaxClasses + threadIdx.x] = acc;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kChunk) void k_predict_final(const int8_t* __restrict__ Q,
+                                                          const int8_t* __restrict__ K,
+                                                          const int8_t* __restrict__ W,
+                                                          const int32_t* __restrict__ tot,
+                                                          int32_t* __restrict__ budget, int T,
+                                                          int nc, int kpc, int cap)
+{
+    __shared__ int wl[kMaxClasses * D / 2];
+    __shared__ int us[kChunk][kMaxClasses + 1];
+    __shared__ int off[kChunk / 32][kMaxClasses + 1];
+    __shared__ int segoff[kChunk / 32][kMaxClasses + 1];
+    const int nch = (int)chunks_per_pair(T);
+    const int pair = blockIdx.x / nch, chunk = blockIdx.x % nch;
+    stage_weights<D>(W, nc, wl);
+    {   // offset from earlier chunks: thread (lane-group, class) takes a strided share
+        const int c = threadIdx.x % kMaxClasses, grp = threadIdx.x / kMaxClasses;
+        int acc = 0;
+        for (int k = grp; k < chunk; k += kChunk / kMaxClasses)
+            acc += tot[((size_t)pair * nch + k) * kMaxClasses + c];
+        off[grp][c] = acc;
+    }
+    __syncthreads();
+    const int t = chunk * kChunk + threadIdx.x;
+    const bool live = t < T;
+    int u[kMaxClasses];
+    if (live) {
+        int kw[D / 4];
+        const int* kr = reinterpret_cast<const int*>(K + ((size_t)pair * T + t) * D);
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) kw[i] = kr[i];
+        class_dots<D>(kw, wl, nc, D / 4, u);
+    } else {
+#pragma unroll
+        for (int c = 0; c < kMaxClasses; ++c) u[c] = 0;
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) us[threadIdx.x][c] = u[c];
+    __syncthreads();
+    {   // inclusive scan within each 32-position segment, per class
+        const int c = threadIdx.x % kMaxClasses, seg = threadIdx.x / kMaxClasses;
+        int acc = 0;
+        for (int j = 0; j < 32; ++j) {
+            acc += us[seg * 32 + j][c];
+            us[seg * 32 + j][c] = acc;
+        }
+        segoff[seg][c] = acc;
+    }
+    __syncthreads();
+    if (!live) return;
+    const int seg = threadIdx.x / 32;
+    int qw[D / 4];
+    const int* qr = reinterpret_cast<const int*>(Q + ((size_t)pair * T + t) * D);
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) qw[i] = qr[i];
+    int best = 0, best_z = 0;
+    for (int c = 0; c < nc; ++c) {
+        int z = us[threadIdx.x][c];
+        for (int s2 = 0; s2 < seg; ++s2) z += segoff[s2][c];
+        for (int g = 0; g < kChunk / kMaxClasses; ++g) z += off[g][c];
+        const int* w = wl + c * (D / 2);
+        for (int i = 0; i < D / 4; ++i) z = dot4_i8(qw[i], w[i], z);
+        if (c == 0 || z > best_z) {
+            best = c;
+            best_z = z;
+        }
+    }
+    const int b = kpc * (best + 1);
+    budget[(size_t)pair * T + t] = b < cap ? b : cap;
+}
+
+template <int D>
+hipError_t predict_d(const Shape& s, const int8_t* Q, const int8_t* K, const int8_t* W,
+                     int32_t* budget, void* ws, hipStream_t st)
+{
+    const int nch = (int)chunks_per_pair(s.T);
+    int32_t* tot = static_cast<int32_t*>(ws);
+    const dim3 grid((unsigned)(s.P * nch));
+    hipLaunchKernelGGL((k_predict_chunks<D>), grid, dim3(kChunk), 0, st, K, W, tot, s.T,
+                       s.n_classes);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_predict_final<D>), grid, dim3(kChunk), 0, st, Q, K, W,
+                       (const int32_t*)tot, budget, s.T, s.n_classes, s.keys_per_class,
+                       s.max_budget);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t predict_ws_bytes(const Shape& s)
+{
+    const size_t b = (size_t)s.P * chunks_per_pair(s.T) * kMaxClasses * sizeof(int32_t);
+    return (b + 255) / 256 * 256;
+}
+
+hipError_t launch_predict(const Shape& s, const int8_t* Q, const int8_t* K, const int8_t* W,
+                          int32_t* budget, void* ws, hipStream_t st)
+{
+    switch (s.d) {
+        case 16: return predict_d<16>(s, Q, K, W, budget, ws, st);
+        case 32: return predict_d<32>(s, Q, K, W, budget, ws, st);
+        case 64: return predict_d<64>(s, Q, K, W, budget, ws, st);
+        case 128: return predict_d<128>(s, Q, K, W, budget, ws, st);
+        case 256: return predict_d<256>(s, Q, K, W, budget, ws, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace alhr

@@ -1,0 +1,621 @@
+// Routing and sparse attention, one wavefront per query (ALHR README,
+// "Inference stage" and "Training stage"; decode use from the openai-hub
+// article "ALHR把注意力变成树搜索", section "ALHR是什么").
+//
+// Per query t with budget B: C = min(B, t+1) keys, the n = min(w, C)
+// neighbours t-n+1..t, and a beam of width r = C - n over the maximal
+// complete subtrees covering [0, m), m = t+1-n.  Each round expands every
+// internal beam node into its two children and keeps the r best candidates
+// by (q . node_sum desc, first position asc); leaves stay in the beam and
+// compete.  The loop ends when the beam holds only leaves.
+//
+// Mapping to gfx950:
+//  * scoring: a tree row (int32 x d) is split over d/16 lanes that each load
+//    4 x 16 B and do 16 multiply-adds; a key row (int8 x d) over the same
+//    lanes with one 16 B load and 4 packed int8 dot ops; a few xor-shuffles
+//    finish the row.  64 / (d/16) rows are scored per pass.
+//  * only the left child of an expanded node is loaded: the right child's
+//    score is the parent's minus the left's (exact in integers), which
+//    halves the gathered tree bytes.
+//  * selection: candidates are 64-bit keys (biased score | inverted start |
+//    level) held 4 per lane; the r-th best score is found by bisection on
+//    wave ballot counts, ties at the threshold by a second bisection on the
+//    start, then a ballot prefix compacts the winners.
+//  * beam, candidates and the final picks live in a 4.5 KiB per-wave LDS
+//    block; the final picks are sorted by counting ranks.
+//  * attention reuses the leaf scores as logits: fp32 softmax, then a gather
+//    of the C value rows with d/4 lanes per row (16 B each).
+#include "device.h"
+#include "kernels.h"
+
+namespace alhr {
+namespace {
+
+constexpr int kMaxBudget = 128;
+constexpr int kSlots = 256;             // 2 * (kMaxBudget - 1) candidates fit
+constexpr int kWavesPerBlock = 4;
+constexpr int kThreads = kWavesPerBlock * kWave;
+constexpr int kMaxClasses = 32;
+
+struct WaveLds {
+    uint64_t beam[kMaxBudget];
+    uint64_t cand[kSlots];
+    int32_t pos[kMaxBudget];
+    int32_t score[kMaxBudget];
+    float w[kMaxBudget];
+};
+
+// ---- candidate keys: larger key = better node ----------------------------
+__device__ __forceinline__ uint64_t make_key(int score, int start, int level)
+{
+    const uint32_t hi = (uint32_t)score ^ 0x80000000u;
+    const uint32_t lo = ((uint32_t)(0xFFFFF - start) << 5) | (uint32_t)level;
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ int key_score(uint64_t k) { return (int)((uint32_t)(k >> 32) ^ 0x80000000u); }
+__device__ __forceinline__ int key_start(uint64_t k) { return 0xFFFFF - (int)((uint32_t)k >> 5); }
+__device__ __forceinline__ int key_level(uint64_t k) { return (int)((uint32_t)k & 31u); }
+
+// ---- the query in registers, in the two column layouts used for scoring ---
+template <int D>
+struct QueryRegs {
+    int qi[16];   // tree-row columns 4*(k*LPR + s) + e  (k, e < 4)
+    int qp[4];    // key-row columns 16*s .. 16*s + 15, packed int8
+};
+
+template <int D>
+__device__ __forceinline__ void load_query(const int8_t* __restrict__ q, int s, QueryRegs<D>& r)
+{
+    constexpr int LPR = D / 16;
+    const int* qw = reinterpret_cast<const int*>(q);
+    const int4 p = reinterpret_cast<const int4*>(q)[s];
+    r.qp[0] = p.x;
+    r.qp[1] = p.y;
+    r.qp[2] = p.z;
+    r.qp[3] = p.w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int w = qw[k * LPR + s];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.qi[4 * k + e] = sbyte(w, e);
+    }
+}
+
+template <bool MUL24>
+__device__ __forceinline__ int imul(int a, int b)
+{
+    if constexpr (MUL24) return __mul24(a, b);
+    else return a * b;
+}
+
+// q . node for node (level, start) of one pair; every lane of the row's
+// group receives the full score.  Inactive lanes contribute 0.
+template <int D, bool MUL24>
+__device__ __forceinline__ int score_node(const int32_t* __restrict__ nodes_pair,
+                                          const int8_t* __restrict__ keys_pair, int T, int level,
+                                          int start, bool active, int s, const QueryRegs<D>& q)
+{
+    constexpr int LPR = D / 16;
+    int acc = 0;
+    if (active) {
+        if (level > 0) {
+            const int4* row = reinterpret_cast<const int4*>(
+                nodes_pair + (size_t)((T >> level) + (start >> level)) * D);
+            int4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = row[k * LPR + s];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                acc += imul<MUL24>(q.qi[4 * k + 0], v[k].x);
+                acc += imul<MUL24>(q.qi[4 * k + 1], v[k].y);
+                acc += imul<MUL24>(q.qi[4 * k + 2], v[k].z);
+                acc += imul<MUL24>(q.qi[4 * k + 3], v[k].w);
+            }
+        } else {
+            const int4 v = reinterpret_cast<const int4*>(keys_pair + (size_t)start * D)[s];
+            acc = dot4_i8(q.qp[0], v.x, acc);
+            acc = dot4_i8(q.qp[1], v.y, acc);
+            acc = dot4_i8(q.qp[2], v.z, acc);
+            acc = dot4_i8(q.qp[3], v.w, acc);
+        }
+    }
+    return group_sum<LPR>(acc);
+}
+
+// Keep the best min(r, #non-empty) keys of cand[0, n) (0 = empty slot) in
+// beam[0, ...); returns how many were kept.  The order of beam is the slot
+// order of the winners (the set is what matters: keys are distinct).
+__device__ int select_best(const uint64_t* cand, int n, int r, uint64_t* beam)
+{
+    const int lane = lane_id();
+    uint64_t k[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int sl = lane + kWave * j;
+        k[j] = (kWave * j < n && sl < n) ? cand[sl] : 0ull;
+    }
+    int nvalid = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) nvalid += wave_count(k[j] != 0ull);
+    bool sel[4];
+    if (nvalid <= r) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sel[j] = k[j] != 0ull;
+    } else {
+        uint32_t h[4];
+        uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            h[j] = (uint32_t)(k[j] >> 32);   // empty slots: 0, below every real key
+            if (k[j] != 0ull) {
+                mx = h[j] > mx ? h[j] : mx;
+                mn = h[j] < mn ? h[j] : mn;
+            }
+        }
+        mx = wave_max(mx);
+        mn = wave_min(mn);
+        // largest threshold with at least r scores >= it
+        uint32_t lo = mn, hb = mx;
+        while (lo < hb) {
+            const uint32_t mid = lo + ((hb - lo + 1u) >> 1);
+            int c = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c += wave_count(h[j] >= mid);
+            if (c >= r) lo = mid;
+            else hb = mid - 1u;
+        }
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            gt += wave_count(h[j] > lo);
+            eq += wave_count(k[j] != 0ull && h[j] == lo);
+        }
+        const int need = r - gt;
+        if (need == eq) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sel[j] = k[j] != 0ull && h[j] >= lo;
+        } else {
+            // ties at the threshold: keep the `need` lowest starts (largest low words)
+            bool tie[4];
+            uint32_t l[4];
+            uint32_t lmx = 0u, lmn = 0xFFFFFFFFu;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                tie[j] = k[j] != 0ull && h[j] == lo;
+                l[j] = (uint32_t)k[j];
+                if (tie[j]) {
+                    lmx = l[j] > lmx ? l[j] : lmx;
+                    lmn = l[j] < lmn ? l[j] : lmn;
+                }
+            }
+            lmx = wave_max(lmx);
+            lmn = wave_min(lmn);
+            uint32_t a = lmn, b = lmx;
+            while (a < b) {
+                const uint32_t mid = a + ((b - a + 1u) >> 1);
+                int c = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) c += wave_count(tie[j] && l[j] >= mid);
+                if (c >= need) a = mid;
+                else b = mid - 1u;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sel[j] = (k[j] != 0ull && h[j] > lo) || (tie[j] && l[j] >= a);
+        }
+    }
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint64_t msk = __ballot(sel[j]);
+        if (sel[j]) beam[base + (int)mbcnt(msk)] = k[j];
+        base += popc64(msk);
+    }
+    return base;
+}
+
+struct RouteCounts {
+    int tree_rows;   // int32 tree rows loaded
+    int key_rows;    // key rows loaded by the descent
+};
+
+// Route query t of one pair.  On return sm.pos[0, C) holds the selected
+// positions in ascending order and sm.score[0, C) their q . K scores.
+template <int D, bool MUL24, bool STATS>
+__device__ int route_query(const int32_t* __restrict__ nodes_pair,
+                           const int8_t* __restrict__ keys_pair, int T, int L, int t, int B,
+                           int window, const QueryRegs<D>& q, WaveLds& sm, RouteCounts& cnt)
+{
+    constexpr int LPR = D / 16, RPG = kWave / LPR;
+    const int lane = lane_id();
+    const int s = lane % LPR, g = lane / LPR;
+    const int C = B < t + 1 ? B : t + 1;
+    const int n = window < C ? window : C;
+    const int r = C - n;
+    const int m = t + 1 - n;
+
+    // neighbours m..t go to slots r.. (they follow every routed key, which is < m)
+    for (int base = 0; base < n; base += RPG) {
+        const int k = base + g;
+        const bool act = k < n;
+        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, 0, m + k, act, s, q);
+        if (act && s == 0) {
+            sm.pos[r + k] = m + k;
+            sm.score[r + k] = sc;
+        }
+    }
+    if (r == 0) {
+        wave_sync();
+        return C;
+    }
+
+    // cover of [0, m): bit l of m set -> node (l, start = m with bits <= l cleared)
+    for (int base = 0; base < L; base += RPG) {
+        const int b = base + g;
+        const bool act = b < L && ((m >> b) & 1);
+        const int start = act ? (m & ~((2 << b) - 1)) : 0;
+        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, b, start, act, s, q);
+        if (STATS) {
+            cnt.tree_rows += wave_count(act && s == 0 && b > 0);
+            cnt.key_rows += wave_count(act && s == 0 && b == 0);
+        }
+        if (b < L && s == 0) sm.cand[b] = act ? make_key(sc, start, b) : 0ull;
+    }
+    wave_sync();
+    int nb = select_best(sm.cand, L, r, sm.beam);
+    wave_sync();
+
+    for (;;) {
+        bool inner = false;
+        for (int i = lane; i < nb; i += kWave) inner |= key_level(sm.beam[i]) > 0;
+        if (!__ballot(inner)) break;
+        for (int base = 0; base < nb; base += RPG) {
+            const int i = base + g;
+            const uint64_t key = i < nb ? sm.beam[i] : 0ull;
+            const int lv = key_level(key), st = key_start(key);
+            const bool expand = i < nb && lv > 0;
+            const int cl = lv - 1;
+            const int left = score_node<D, MUL24>(nodes_pair, keys_pair, T, cl, st, expand, s, q);
+            if (STATS) {
+                cnt.tree_rows += wave_count(expand && s == 0 && cl > 0);
+                cnt.key_rows += wave_count(expand && s == 0 && cl == 0);
+            }
+            if (i < nb && s == 0) {
+                if (expand) {
+                    sm.cand[2 * i] = make_key(left, st, cl);
+                    sm.cand[2 * i + 1] = make_key(key_score(key) - left, st + (1 << cl), cl);
+                } else {
+                    sm.cand[2 * i] = key;
+                    sm.cand[2 * i + 1] = 0ull;
+                }
+            }
+        }
+        wave_sync();
+        nb = select_best(sm.cand, 2 * nb, r, sm.beam);
+        wave_sync();
+    }
+
+    // the r routed keys, in ascending position order, by counting ranks
+    {
+        const uint64_t k0 = lane < r ? sm.beam[lane] : 0ull;
+        const uint64_t k1 = lane + kWave < r ? sm.beam[lane + kWave] : 0ull;
+        const int s0 = key_start(k0), s1 = key_start(k1);
+        int r0 = 0, r1 = 0;
+        for (int j = 0; j < r; ++j) {
+            const int sj = key_start(sm.beam[j]);
+            r0 += sj < s0;
+            r1 += sj < s1;
+        }
+        if (lane < r) {
+            sm.pos[r0] = s0;
+            sm.score[r0] = key_score(k0);
+        }
+        if (lane + kWave < r) {
+            sm.pos[r1] = s1;
+            sm.score[r1] = key_score(k1);
+        }
+    }
+    wave_sync();
+    return C;
+}
+
+__device__ __forceinline__ void write_selection(const WaveLds& sm, int C, int max_budget,
+                                                int32_t* __restrict__ idx_row,
+                                                int32_t* __restrict__ count_out)
+{
+    const int lane = lane_id();
+    for (int c = lane; c < max_budget; c += kWave) idx_row[c] = c < C ? sm.pos[c] : -1;
+    if (lane == 0) *count_out = C;
+}
+
+// softmax over sm.score[0, C) * scale and the weighted sum of value rows.
+// Positions outside [0, T) (possible only in caller-supplied index sets) are
+// left out of the softmax and never loaded; with none left the output is 0.
+template <int D>
+__device__ void attend_selected(WaveLds& sm, int C, int T, float scale,
+                                const float* __restrict__ values_pair, float* __restrict__ out)
+{
+    constexpr int LPV = D / 4, RPV = kWave / LPV;
+    const int lane = lane_id();
+    const bool ok0 = lane < C && (unsigned)sm.pos[lane] < (unsigned)T;
+    const bool ok1 = lane + kWave < C && (unsigned)sm.pos[lane + kWave] < (unsigned)T;
+    const float a0 = ok0 ? (float)sm.score[lane] * scale : -INFINITY;
+    const float a1 = ok1 ? (float)sm.score[lane + kWave] * scale : -INFINITY;
+    const float mx = wave_max(a0 > a1 ? a0 : a1);
+    const float e0 = ok0 ? __expf(a0 - mx) : 0.0f;
+    const float e1 = ok1 ? __expf(a1 - mx) : 0.0f;
+    if (lane < C) sm.w[lane] = e0;
+    if (lane + kWave < C) sm.w[lane + kWave] = e1;
+    const float z = wave_sum(e0 + e1);
+    wave_sync();
+    const int cv = lane % LPV, rv = lane / LPV;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = rv; c < C; c += RPV) {
+        const int j = sm.pos[c];
+        if ((unsigned)j >= (unsigned)T) continue;
+        const float wt = sm.w[c];
+        const float4 v = reinterpret_cast<const float4*>(values_pair + (size_t)j * D)[cv];
+        acc.x += wt * v.x;
+        acc.y += wt * v.y;
+        acc.z += wt * v.z;
+        acc.w += wt * v.w;
+    }
+#pragma unroll
+    for (int o = LPV; o < kWave; o <<= 1) {
+        acc.x += __shfl_xor(acc.x, o);
+        acc.y += __shfl_xor(acc.y, o);
+        acc.z += __shfl_xor(acc.z, o);
+        acc.w += __shfl_xor(acc.w, o);
+    }
+    if (rv == 0) {
+        const float inv = z > 0.0f ? 1.0f / z : 0.0f;
+        reinterpret_cast<float4*>(out)[cv] =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+}
+
+// ---- prefill: one wave per (pair, t), expensive (late) queries first -----
+template <int D, bool MUL24, bool ATTEND, bool STATS>
+__global__ __launch_bounds__(kThreads) void k_route(
+    const int8_t* __restrict__ Q, const int8_t* __restrict__ K, const float* __restrict__ V,
+    const int32_t* __restrict__ nodes, const int32_t* __restrict__ budget, int fixed_budget,
+    int32_t* __restrict__ idx, int32_t* __restrict__ count, float* __restrict__ O,
+    int32_t* __restrict__ stats, int P, int T, int L, int window, int max_budget, float scale)
+{
+    __shared__ WaveLds smem[kWavesPerBlock];
+    const int wid = threadIdx.x / kWave;
+    const uint64_t gw = (uint64_t)xcd_logical_block() * kWavesPerBlock + wid;
+    if (gw >= (uint64_t)P * T) return;
+    const int pair = (int)(gw / (uint64_t)T);
+    const int t = T - 1 - (int)(gw % (uint64_t)T);
+    const size_t qrow = (size_t)pair * T + t;
+    const int s = lane_id() % (D / 16);
+    QueryRegs<D> q;
+    load_query<D>(Q + qrow * D, s, q);
+    // budgets outside [1, max_budget] are clamped: the beam and idx rows hold max_budget
+    int B = budget ? budget[qrow] : fixed_budget;
+    B = B < 1 ? 1 : (B > max_budget ? max_budget : B);
+    WaveLds& sm = smem[wid];
+    RouteCounts cnt{0, 0};
+    const int C = route_query<D, MUL24, STATS>(nodes + (size_t)pair * T * D,
+                                                K + (size_t)pair * T * D, T, L, t, B, window, q,
+                                                sm, cnt);
+    write_selection(sm, C, max_budget, idx + qrow * max_budget, count + qrow);
+    if (STATS && lane_id() == 0) {
+        const int n = window < C ? window : C;
+        stats[qrow * 4 + 0] = cnt.tree_rows;
+        stats[qrow * 4 + 1] = cnt.key_rows;
+        stats[qrow * 4 + 2] = n;
+        stats[qrow * 4 + 3] = C;
+    }
+    if constexpr (ATTEND)
+        attend_selected<D>(sm, C, T, scale, V + (size_t)pair * T * D, O + qrow * D);
+}
+
+// ---- attention over given index sets -------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_attend(const int8_t* __restrict__ Q,
+                                                     const int8_t* __restrict__ K,
+                                                     const float* __restrict__ V,
+                                                     const int32_t* __restrict__ idx,
+                                                     const int32_t* __restrict__ count,
+                                                     float* __restrict__ O, int P, int T,
+                                                     int max_budget, float scale)
+{
+    constexpr int LPR = D / 16, RPG = kWave / LPR;
+    __shared__ WaveLds smem[kWavesPerBlock];
+    const int wid = threadIdx.x / kWave;
+    const uint64_t gw = (uint64_t)xcd_logical_block() * kWavesPerBlock + wid;
+    if (gw >= (uint64_t)P * T) return;
+    const int pair = (int)(gw / (uint64_t)T);
+    const int t = (int)(gw % (uint64_t)T);
+    const size_t qrow = (size_t)pair * T + t;
+    const int lane = lane_id(), s = lane % LPR, g = lane / LPR;
+    QueryRegs<D> q;
+    load_query<D>(Q + qrow * D, s, q);
+    WaveLds& sm = smem[wid];
+    // caller-supplied sets: count is clamped to [0, max_budget], positions
+    // outside [0, T) are skipped
+    int C = count[qrow];
+    C = C < 0 ? 0 : (C > max_budget ? max_budget : C);
+    const int8_t* keys_pair = K + (size_t)pair * T * D;
+    for (int base = 0; base < C; base += RPG) {
+        const int c = base + g;
+        const int j = c < C ? idx[qrow * max_budget + c] : -1;
+        const bool act = c < C && (unsigned)j < (unsigned)T;
+        const int sc = score_node<D, false>(nullptr, keys_pair, T, 0, act ? j : 0, act, s, q);
+        if (c < C && s == 0) {
+            sm.pos[c] = j;
+            sm.score[c] = sc;
+        }
+    }
+    wave_sync();
+    attend_selected<D>(sm, C, T, scale, V + (size_t)pair * T * D, O + qrow * D);
+}
+
+// ---- decode: one wave per pair, query at position pos --------------------
+// Budget from W . [q; S[pos]]: lane c < n_classes forms z_c, then an argmax
+// over (z, lowest class) keys.
+template <int D>
+__device__ __forceinline__ int predict_one(const int8_t* __restrict__ q,
+                                           const int32_t* __restrict__ pre,
+                                           const int8_t* __restrict__ W, int nc, int kpc, int cap)
+{
+    const int lane = lane_id();
+    int z = 0;
+    if (lane < nc) {
+        const int* w = reinterpret_cast<const int*>(W + (size_t)lane * 2 * D);
+        const int* qw = reinterpret_cast<const int*>(q);
+        for (int i = 0; i < D / 4; ++i) z = dot4_i8(w[i], qw[i], z);
+        for (int i = 0; i < D / 4; ++i) {
+            const int ws = w[D / 4 + i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z += sbyte(ws, e) * pre[4 * i + e];
+        }
+    }
+    const uint64_t key = lane < nc ? (((uint64_t)((uint32_t)z ^ 0x80000000u) << 32) |
+                                      (uint32_t)(kMaxClasses - lane))
+                                   : 0ull;
+    const uint64_t best = wave_max(key);
+    const int cls = kMaxClasses - (int)(uint32_t)best;
+    const int b = kpc * (cls + 1);
+    return b < cap ? b : cap;
+}
+
+template <int D, bool MUL24>
+__global__ __launch_bounds__(kThreads) void k_decode(
+    const int8_t* __restrict__ q_new, const int8_t* __restrict__ K, const float* __restrict__ V,
+    const int32_t* __restrict__ nodes, const int32_t* __restrict__ prefix,
+    const int8_t* __restrict__ W, int fixed_budget, int32_t* __restrict__ budget_out,
+    int32_t* __restrict__ idx, int32_t* __restrict__ count, float* __restrict__ O, int P, int T,
+    int L, int pos, int window, int nc, int kpc, int max_budget, float scale)
+{
+    __shared__ WaveLds smem[kWavesPerBlock];
+    const int wid = threadIdx.x / kWave;
+    const uint64_t gw = (uint64_t)xcd_logical_block() * kWavesPerBlock + wid;
+    if (gw >= (uint64_t)P) return;
+    const int pair = (int)gw;
+    const int s = lane_id() % (D / 16);
+    const int8_t* qp = q_new + (size_t)pair * D;
+    QueryRegs<D> q;
+    load_query<D>(qp, s, q);
+    const int B = W ? predict_one<D>(qp, prefix + (size_t)pair * D, W, nc, kpc, max_budget)
+                    : fixed_budget;
+    if (budget_out && lane_id() == 0) budget_out[pair] = B;
+    WaveLds& sm = smem[wid];
+    RouteCounts cnt{0, 0};
+    const int C = route_query<D, MUL24, false>(nodes + (size_t)pair * T * D,
+                                                K + (size_t)pair * T * D, T, L, pos, B, window,
+                                                q, sm, cnt);
+    write_selection(sm, C, max_budget, idx + (size_t)pair * max_budget, count + pair);
+    attend_selected<D>(sm, C, T, scale, V + (size_t)pair * T * D, O + (size_t)pair * D);
+}
+
+unsigned grid_for_waves(uint64_t waves)
+{
+    uint64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    blocks = (blocks + kXcds - 1) / kXcds * kXcds;   // xcd_logical_block needs a multiple
+    return (unsigned)blocks;
+}
+
+template <int D, bool MUL24>
+hipError_t route_d(const Shape& s, const int8_t* Q, const int8_t* K, const float* V,
+                   const int32_t* nodes, const int32_t* budget, int fixed_budget, int32_t* idx,
+                   int32_t* count, float* O, int32_t* stats, hipStream_t st)
+{
+    const dim3 grid(grid_for_waves((uint64_t)s.P * s.T));
+    if (stats)
+        hipLaunchKernelGGL((k_route<D, MUL24, false, true>), grid, dim3(kThreads), 0, st, Q, K, V,
+                           nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T, s.L,
+                           s.window, s.max_budget, s.scale);
+    else if (O)
+        hipLaunchKernelGGL((k_route<D, MUL24, true, false>), grid, dim3(kThreads), 0, st, Q, K, V,
+                           nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T, s.L,
+                           s.window, s.max_budget, s.scale);
+    else
+        hipLaunchKernelGGL((k_route<D, MUL24, false, false>), grid, dim3(kThreads), 0, st, Q, K,
+                           V, nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T, s.L,
+                           s.window, s.max_budget, s.scale);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t route_dispatch(const Shape& s, const int8_t* Q, const int8_t* K, const float* V,
+                          const int32_t* nodes, const int32_t* budget, int fixed_budget,
+                          int32_t* idx, int32_t* count, float* O, int32_t* stats, hipStream_t st)
+{
+    return s.mul24 ? route_d<D, true>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O,
+                                      stats, st)
+                   : route_d<D, false>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O,
+                                       stats, st);
+}
+
+template <int D>
+hipError_t decode_d(const Shape& s, int pos, const int8_t* q_new, const int8_t* K,
+                    const float* V, const int32_t* nodes, const int32_t* prefix, const int8_t* W,
+                    int fixed_budget, int32_t* budget, int32_t* idx, int32_t* count, float* O,
+                    hipStream_t st)
+{
+    const dim3 grid(grid_for_waves((uint64_t)s.P));
+    if (s.mul24)
+        hipLaunchKernelGGL((k_decode<D, true>), grid, dim3(kThreads), 0, st, q_new, K, V, nodes,
+                           prefix, W, fixed_budget, budget, idx, count, O, s.P, s.T, s.L, pos,
+                           s.window, s.n_classes, s.keys_per_class, s.max_budget, s.scale);
+    else
+        hipLaunchKernelGGL((k_decode<D, false>), grid, dim3(kThreads), 0, st, q_new, K, V, nodes,
+                           prefix, W, fixed_budget, budget, idx, count, O, s.P, s.T, s.L, pos,
+                           s.window, s.n_classes, s.keys_per_class, s.max_budget, s.scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(const Shape& s, const int8_t* Q, const int8_t* K, const float* V,
+                        const int32_t* nodes, const int32_t* budget, int fixed_budget,
+                        int32_t* idx, int32_t* count, float* O, int32_t* stats, hipStream_t st)
+{
+    switch (s.d) {
+        case 16: return route_dispatch<16>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O, stats, st);
+        case 32: return route_dispatch<32>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O, stats, st);
+        case 64: return route_dispatch<64>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O, stats, st);
+        case 128: return route_dispatch<128>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O, stats, st);
+        case 256: return route_dispatch<256>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O, stats, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_attend(const Shape& s, const int8_t* Q, const int8_t* K, const float* V,
+                         const int32_t* idx, const int32_t* count, float* O, hipStream_t st)
+{
+    const dim3 grid(grid_for_waves((uint64_t)s.P * s.T));
+#define ALHR_ATTEND(DD)                                                                          \
+    hipLaunchKernelGGL((k_attend<DD>), grid, dim3(kThreads), 0, st, Q, K, V, idx, count, O, s.P, \
+                       s.T, s.max_budget, s.scale)
+    switch (s.d) {
+        case 16: ALHR_ATTEND(16); break;
+        case 32: ALHR_ATTEND(32); break;
+        case 64: ALHR_ATTEND(64); break;
+        case 128: ALHR_ATTEND(128); break;
+        case 256: ALHR_ATTEND(256); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef ALHR_ATTEND
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const Shape& s, int pos, const int8_t* q_new, const int8_t* K,
+                         const float* V, const int32_t* nodes, const int32_t* prefix,
+                         const int8_t* W, int fixed_budget, int32_t* budget, int32_t* idx,
+                         int32_t* count, float* O, hipStream_t st)
+{
+    switch (s.d) {
+        case 16: return decode_d<16>(s, pos, q_new, K, V, nodes, prefix, W, fixed_budget, budget, idx, count, O, st);
+        case 32: return decode_d<32>(s, pos, q_new, K, V, nodes, prefix, W, fixed_budget, budget, idx, count, O, st);
+        case 64: return decode_d<64>(s, pos, q_new, K, V, nodes, prefix, W, fixed_budget, budget, idx, count, O, st);
+        case 128: return decode_d<128>(s, pos, q_new, K, V, nodes, prefix, W, fixed_budget, budget, idx, count, O, st);
+        case 256: return decode_d<256>(s, pos, q_new, K, V, nodes, prefix, W, fixed_budget, budget, idx, count, O, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace alhr

@@ -12,6 +12,7 @@ Each function works on one (batch, head) pair with host numpy arrays:
     route(t, budget, q, K, nodes, window, cap) -> (idx[cap], scores[cap], count, stats)
     attend(idx[:C], q, K, V, scale)            -> fp32 [d]
     pair_forward(...)        -> dict of per-query outputs
+    pair_budgets(Q, K, W)    -> int32 [T] predicted budgets
     append(p, k, v, K, V, nodes, prefix)       (in place)
 """
 from __future__ import annotations
@@ -76,6 +77,8 @@ def _load():
     lib.alhr_ref_pair_forward.argtypes = [i32, i32, i32, i32, i32, i32, dbl, P, P, P, P, i32,
                                           P, i32, P, P, P, i32, P, P, P, P]
     lib.alhr_ref_pair_forward.restype = C.c_int
+    lib.alhr_ref_pair_budgets.argtypes = [i32, i32, P, P, P, i32, i32, i32, P, P]
+    lib.alhr_ref_pair_budgets.restype = C.c_int
     lib.alhr_ref_append.argtypes = [i32, i32, i32, P, P, P, P, P, P]
     lib.alhr_ref_append.restype = C.c_int
     _lib = lib
@@ -192,6 +195,21 @@ def pair_forward(Q, K, V, W=None, fixed_budget=16, window=4, n_classes=32,
         out["S"] = S
     if with_stats:
         out["stats"] = [s.as_dict() for s in stats]
+    return out
+
+
+def pair_budgets(Q, K, W, keys_per_class=3, max_budget=96):
+    """Predicted budget of every query of one pair."""
+    Q = _c(Q, np.int8)
+    K = _c(K, np.int8)
+    W = _c(W, np.int8)
+    T, d = K.shape
+    S = np.zeros((T, d), dtype=np.int64)
+    out = np.zeros(T, dtype=np.int32)
+    rc = _load().alhr_ref_pair_budgets(T, d, _p(Q), _p(K), _p(W), W.shape[0], keys_per_class,
+                                       max_budget, _p(S), _p(out))
+    if rc:
+        raise ValueError("alhr_ref_pair_budgets failed: %d" % rc)
     return out
 
 

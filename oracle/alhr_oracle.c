@@ -376,3 +376,19 @@ int alhr_ref_append(int32_t T, int32_t d, int32_t p, const int8_t *k_new,
         for (int i = 0; i < d; ++i) prefix[i] += k_new[i];
     return REF_OK;
 }
+
+/* Budgets of every query of one pair: O2 then O3 for t = 0..T-1. */
+int alhr_ref_pair_budgets(int32_t T, int32_t d, const int8_t *Q, const int8_t *K,
+                          const int8_t *W, int32_t n_classes, int32_t keys_per_class,
+                          int32_t max_budget, int64_t *S, int32_t *budget)
+{
+    int rc = alhr_ref_prefix(T, d, K, S);
+    if (rc) return rc;
+    for (int64_t t = 0; t < T; ++t) {
+        int32_t b = alhr_ref_budget(d, Q + t * d, S + t * d, W, n_classes, keys_per_class,
+                                    max_budget, NULL);
+        if (b < 1) return REF_ERR_ARG;
+        budget[t] = b;
+    }
+    return REF_OK;
+}

@@ -1,0 +1,205 @@
+"""GPU parity of the decode path (append + decode step) and of the device
+input generator.
+
+The decode oracle replays the same appends on the CPU for a pair and routes
+and attends the one query per step; tree rows, budgets, index sets and
+counts must match bit for bit, outputs within 1e-4.  The full-size cache
+(64 sequences x 16 heads, 2^17 positions, d = 128; 144 GiB of keys, values
+and tree) is generated on the device and checked on sampled pairs.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.workloads import WORKLOADS, Workload, host_inputs, pair_keys, pair_query_rows, pair_value_rows
+
+pytestmark = pytest.mark.gpu
+ATOL = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    return torch, torch.device("cuda:0")
+
+
+def test_device_generator_matches_host(torch_dev):
+    from synth import device as sd
+    torch, dev = torch_dev
+    w = WORKLOADS["t1k"]
+    say("device generator vs host, t1k slice")
+    Q, K, V, W = host_inputs(w, t0=100, nt=300, B=3, H=5)
+    k = sd.keys_(torch.zeros((3, 5, 300, 64), dtype=torch.int8, device=dev), w.seed, 100)
+    q = sd.queries_(torch.zeros((3, 5, 300, 64), dtype=torch.int8, device=dev), w.seed, 100)
+    v = sd.values_(torch.zeros((3, 5, 300, 64), dtype=torch.float32, device=dev), w.seed, 100)
+    wt = sd.weights_(torch.zeros((32, 128), dtype=torch.int8, device=dev), w.seed)
+    u = sd.uniform_i8_(torch.zeros((3, 5, 300, 64), dtype=torch.int8, device=dev), 1,
+                       synth.STREAM_UK, -4, 4, 100)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(k.cpu().numpy(), K)
+    np.testing.assert_array_equal(q.cpu().numpy(), Q)
+    np.testing.assert_array_equal(v.cpu().numpy(), V)
+    np.testing.assert_array_equal(wt.cpu().numpy(), W)
+    np.testing.assert_array_equal(u.cpu().numpy(),
+                                  synth.uniform_i8(1, synth.STREAM_UK, -4, 4, 3, 5, 64, 100, 300))
+    # strided rows (prefix of a larger cache), the rest untouched
+    big = torch.zeros((2, 3, 64, 64), dtype=torch.int8, device=dev)
+    sd.keys_(big, w.seed, 0, 40)
+    torch.cuda.synchronize()
+    b = big.cpu().numpy()
+    np.testing.assert_array_equal(b[:, :, :40], synth.clustered_keys(w.seed, 2, 3, 64, 0, 40))
+    assert not b[:, :, 40:].any()
+
+
+def decode_oracle_pair(w, b, h, n0, steps, K_pair, q_rows, W, cfg):
+    """Replays the decode steps of one pair on the CPU; returns per-step
+    (budget, idx, count, O) and the final tree and prefix."""
+    Kc = np.zeros_like(K_pair)
+    Kc[:n0] = K_pair[:n0]
+    V = np.zeros((w.T, w.d), np.float32)
+    have = np.zeros(w.T, dtype=bool)          # value rows drawn so far
+    nodes = oracle.build_tree(Kc)
+    pre = Kc.astype(np.int64).sum(axis=0)
+    res = []
+    for s in range(steps):
+        p = n0 + s
+        v_new = pair_value_rows(w, b, h, [p])[0]
+        oracle.append(p, K_pair[p], v_new, Kc, V, nodes, pre)
+        have[p] = True
+        q = q_rows[s]
+        if W is not None:
+            bud, _ = oracle.budget(q, pre, W, cfg.keys_per_class, cfg.max_budget)
+        else:
+            bud = w.fixed_budget
+        idx, _, c, _ = oracle.route(p, bud, q, Kc, nodes, cfg.window, cfg.max_budget)
+        need = idx[:c]
+        missing = need[~have[need]]
+        if len(missing):
+            V[missing] = pair_value_rows(w, b, h, missing)
+            have[missing] = True
+        o = oracle.attend(need, q, Kc, V, cfg.scale)
+        res.append((bud, idx, c, o))
+    return res, nodes, pre
+
+
+def run_decode(torch, dev, w, cfg, K_dev, V_dev, nodes, prefix, W_dev, n0, steps, pairs,
+               q_src, k_src, v_src):
+    import learned_tree_routed_amd as alhr
+    got = {pr: [] for pr in pairs}
+    bsel = torch.tensor([p[0] for p in pairs], device=dev)
+    hsel = torch.tensor([p[1] for p in pairs], device=dev)
+    for s in range(steps):
+        p = n0 + s
+        k_new, v_new, q_new = k_src(p), v_src(p), q_src(p)
+        alhr.alhr_append(cfg, p, k_new, v_new, K_dev, V_dev, nodes, prefix)
+        bud = torch.empty((cfg.batch, cfg.heads), dtype=torch.int32, device=dev)
+        idx, cnt, O = alhr.alhr_decode_step(cfg, p, q_new, K_dev, V_dev, nodes, prefix, W_dev,
+                                            fixed_budget=w.fixed_budget, budget=bud)
+        sb, si, sc, so = (bud[bsel, hsel].cpu().numpy(), idx[bsel, hsel].cpu().numpy(),
+                          cnt[bsel, hsel].cpu().numpy(), O[bsel, hsel].cpu().numpy())
+        for k, pr in enumerate(pairs):
+            got[pr].append((sb[k], si[k], sc[k], so[k]))
+    torch.cuda.synchronize()
+    return got
+
+
+def compare(got, ref):
+    assert len(got) == len(ref) > 0
+    for s, ((gb, gi, gc, go), (rb, ri, rc, ro)) in enumerate(zip(got, ref)):
+        assert gb == rb, "step %d: budget %d vs %d" % (s, gb, rb)
+        assert gc == rc, "step %d: count %d vs %d" % (s, gc, rc)
+        np.testing.assert_array_equal(gi, ri, err_msg="step %d" % s)
+        err = np.abs(go - ro).max()
+        assert err <= ATOL, "step %d: max |O - oracle| = %g" % (s, err)
+
+
+@pytest.mark.parametrize("d,fixed", [(128, 0), (64, 0), (32, 20)])
+def test_decode_small_every_step(torch_dev, d, fixed):
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    T, n0, steps = 4096, 4096 - 48, 48
+    w = Workload("decode_small", 7, 2, 3, T, d, "clustered", fixed_budget=fixed)
+    cfg = w.config()
+    Q, K, V, W = host_inputs(w)
+    say("decode small: B2 H3 T%d d%d, %d steps" % (T, d, steps))
+    Kd = torch.zeros((2, 3, T, d), dtype=torch.int8, device=dev)
+    Vd = torch.zeros((2, 3, T, d), dtype=torch.float32, device=dev)
+    Kd[:, :, :n0] = torch.from_numpy(K[:, :, :n0]).to(dev)
+    Vd[:, :, :n0] = torch.from_numpy(V[:, :, :n0]).to(dev)
+    nodes = alhr.alhr_build_tree(cfg, Kd)
+    prefix = alhr.alhr_prefix_from_tree(cfg, n0, Kd, nodes)
+    Wd = None if W is None else torch.from_numpy(W).to(dev)
+    Kh, Vh, Qh = (torch.from_numpy(x).to(dev) for x in (K, V, Q))
+    pairs = [(b, h) for b in range(2) for h in range(3)]
+    got = run_decode(torch, dev, w, cfg, Kd, Vd, nodes, prefix, Wd, n0, steps, pairs,
+                     lambda p: Qh[:, :, p].contiguous(), lambda p: Kh[:, :, p].contiguous(),
+                     lambda p: Vh[:, :, p].contiguous())
+    for (b, h) in pairs:
+        ref, ref_nodes, ref_pre = decode_oracle_pair(w, b, h, n0, steps, K[b, h], Q[b, h, n0:], W, cfg)
+        compare(got[(b, h)], ref)
+        np.testing.assert_array_equal(nodes[b, h, 1:].cpu().numpy(), ref_nodes[1:])
+        np.testing.assert_array_equal(prefix[b, h].cpu().numpy(), ref_pre)
+    # after the appends, the tree equals a fresh build of the full keys
+    rebuilt = alhr.alhr_build_tree(cfg, Kh)
+    torch.cuda.synchronize()
+    assert torch.equal(rebuilt[:, :, 1:], nodes[:, :, 1:])
+    # and the decode rows equal the prefill rows of the same positions
+    full = alhr.alhr_forward(cfg, Qh, Kh, Vh, Wd, fixed_budget=fixed)
+    torch.cuda.synchronize()
+    for (b, h) in pairs:
+        last = got[(b, h)][-1]
+        np.testing.assert_array_equal(last[1], full["idx"][b, h, T - 1].cpu().numpy())
+
+
+def test_decode_full_cache_sampled_pairs(torch_dev):
+    """64 x 16 pairs, capacity 2^17, d = 128, 2^17 - 128 prefilled keys and
+    128 appended tokens: every step compared on 8 sampled pairs."""
+    import learned_tree_routed_amd as alhr
+    from synth import device as sd
+    torch, dev = torch_dev
+    w = WORKLOADS["decode"]
+    cfg = w.config()
+    B, H, T, d, n0, steps = w.B, w.H, w.T, w.d, w.n0, w.steps
+    say("decode full cache: B%d H%d T%d d%d n0=%d steps=%d (144 GiB)" % (B, H, T, d, n0, steps))
+    Kd = torch.zeros((B, H, T, d), dtype=torch.int8, device=dev)
+    Vd = torch.zeros((B, H, T, d), dtype=torch.float32, device=dev)
+    nodes = torch.empty((B, H, T, d), dtype=torch.int32, device=dev)
+    sd.keys_(Kd, w.seed, 0, n0)
+    sd.values_(Vd, w.seed, 0, n0)
+    alhr.alhr_build_tree(cfg, Kd, nodes)
+    prefix = alhr.alhr_prefix_from_tree(cfg, n0, Kd, nodes)
+    Wd = sd.weights_(torch.empty((32, 2 * d), dtype=torch.int8, device=dev), w.seed)
+    kbuf = torch.empty((B, H, 1, d), dtype=torch.int8, device=dev)
+    qbuf = torch.empty((B, H, 1, d), dtype=torch.int8, device=dev)
+    vbuf = torch.empty((B, H, 1, d), dtype=torch.float32, device=dev)
+    rng = np.random.default_rng(w.seed)
+    pairs = sorted({(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(8)})
+    pairs = [(0, 0), (B - 1, H - 1)] + [p for p in pairs if p not in ((0, 0), (B - 1, H - 1))][:6]
+    got = run_decode(torch, dev, w, cfg, Kd, Vd, nodes, prefix, Wd, n0, steps, pairs,
+                     lambda p: sd.queries_(qbuf, w.seed, p, 1).view(B, H, d),
+                     lambda p: sd.keys_(kbuf, w.seed, p, 1).view(B, H, d),
+                     lambda p: sd.values_(vbuf, w.seed, p, 1).view(B, H, d))
+    say("decode full cache: device steps done, oracle replay of %d pairs" % len(pairs))
+    import time
+    t_replay = time.time()
+    W = synth.predictor_weights(w.seed, w.n_classes, d)
+    for (b, h) in pairs:
+        K_pair = pair_keys(w, b, h)
+        q_rows = pair_query_rows(w, b, h, np.arange(n0, n0 + steps))
+        ref, ref_nodes, ref_pre = decode_oracle_pair(w, b, h, n0, steps, K_pair, q_rows, W, cfg)
+        compare(got[(b, h)], ref)
+        np.testing.assert_array_equal(prefix[b, h].cpu().numpy(), ref_pre)
+        top = nodes[b, h, 1:4096].cpu().numpy()
+        np.testing.assert_array_equal(top, ref_nodes[1:4096])
+    say("decode full cache: replayed %d pairs x %d steps in %.1f s" % (len(pairs), steps,
+                                                                   time.time() - t_replay))
+    del Kd, Vd, nodes
+    torch.cuda.empty_cache()

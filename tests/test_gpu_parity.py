@@ -1,0 +1,295 @@
+"""GPU parity: every entry point of libalhr, called through the C ABI (the
+ctypes binding), against the CPU oracle on the same seeded inputs.
+
+Bars: tree rows, budgets, selected index sets and counts bit-exact; the fp32
+attention output within max-abs 1e-4 of the oracle's fp64 result rounded to
+fp32.  Small cases are compared element by element for every query; the
+full-size workloads are compared on sampled queries (each the oracle routes
+one by one), with the tree and the budgets compared in full.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.workloads import WORKLOADS, Workload, host_inputs
+
+pytestmark = pytest.mark.gpu
+ATOL = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    return torch, torch.device("cuda:0")
+
+
+def to_dev(torch, dev, *arrays):
+    return [None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+            for a in arrays]
+
+
+def run_forward(torch, dev, w: Workload, Q, K, V, W, cfg=None, fixed=None):
+    import learned_tree_routed_amd as alhr
+    cfg = cfg or w.config()
+    q, k, v, wt = to_dev(torch, dev, Q, K, V, W)
+    fb = fixed if fixed is not None else w.fixed_budget
+    say("alhr_forward", w.name, "B%d H%d T%d d%d" % (cfg.batch, cfg.heads, cfg.T, cfg.d),
+        "fixed" if wt is None else "predictor")
+    out = alhr.alhr_forward(cfg, q, k, v, wt, fixed_budget=fb)
+    torch.cuda.synchronize()
+    return {k2: (None if t is None else t.cpu().numpy()) for k2, t in out.items()}
+
+
+def check_pair(w, cfg, Q, K, V, W, out, b, h, ts=None, fixed=None):
+    fb = fixed if fixed is not None else w.fixed_budget
+    ref = oracle.pair_forward(Q[b, h], K[b, h], V[b, h], W=W, fixed_budget=fb,
+                              window=cfg.window, keys_per_class=cfg.keys_per_class,
+                              max_budget=cfg.max_budget, scale=cfg.scale, ts=ts)
+    sel = slice(None) if ts is None else np.asarray(ts)
+    if W is not None:
+        np.testing.assert_array_equal(out["budget"][b, h][sel], ref["budget"])
+    np.testing.assert_array_equal(out["count"][b, h][sel], ref["count"])
+    np.testing.assert_array_equal(out["idx"][b, h][sel], ref["idx"])
+    err = np.abs(out["O"][b, h][sel] - ref["O"]).max()
+    assert err <= ATOL, "pair (%d, %d): max |O - oracle| = %g" % (b, h, err)
+    return ref
+
+
+def check_nodes(out_nodes, K, b, h):
+    ref = oracle.build_tree(K[b, h])
+    np.testing.assert_array_equal(out_nodes[b, h][1:], ref[1:])
+
+
+# ------------------------------------------------------------ full parity --
+def test_tiny_every_query(torch_dev):
+    torch, dev = torch_dev
+    w = WORKLOADS["tiny"]
+    Q, K, V, W = host_inputs(w)
+    out = run_forward(torch, dev, w, Q, K, V, W)
+    check_nodes(out["nodes"], K, 0, 0)
+    check_pair(w, w.config(), Q, K, V, W, out, 0, 0)
+
+
+def test_t1k_every_query(torch_dev):
+    torch, dev = torch_dev
+    w = WORKLOADS["t1k"]
+    Q, K, V, W = host_inputs(w)
+    out = run_forward(torch, dev, w, Q, K, V, W)
+    cfg = w.config()
+    for b in range(w.B):
+        for h in range(w.H):
+            check_nodes(out["nodes"], K, b, h)
+            np.testing.assert_array_equal(out["budget"][b, h], oracle.pair_budgets(Q[b, h], K[b, h], W))
+    for b, h in [(0, 0), (3, 5), (7, 7), (5, 2)]:
+        check_pair(w, cfg, Q, K, V, W, out, b, h)
+
+
+# ------------------------------------------------------- sampled, full size --
+def sample_ts(T, rng, n=384):
+    ts = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    ts |= set(range(min(8, T))) | set(range(T - 8, T))
+    return np.array(sorted(ts), dtype=np.int32)
+
+
+@pytest.mark.parametrize("name", ["t4k", "t16k"])
+def test_full_size_sampled(torch_dev, name):
+    torch, dev = torch_dev
+    w = WORKLOADS[name]
+    Q, K, V, W = host_inputs(w)
+    out = run_forward(torch, dev, w, Q, K, V, W)
+    cfg = w.config()
+    rng = np.random.default_rng(w.seed)
+    for b in range(w.B):
+        for h in range(w.H):
+            check_nodes(out["nodes"], K, b, h)
+            np.testing.assert_array_equal(out["budget"][b, h], oracle.pair_budgets(Q[b, h], K[b, h], W))
+            check_pair(w, cfg, Q, K, V, W, out, b, h, ts=sample_ts(w.T, rng, 192))
+    # every query: size = min(budget, t+1), ascending, own key included, -1 padding
+    t = np.arange(w.T)
+    C = out["count"]
+    np.testing.assert_array_equal(C, np.minimum(out["budget"], t + 1))
+    idx = out["idx"]
+    pad = np.arange(w.max_budget)[None, None, None, :] >= C[..., None]
+    assert np.all(idx[pad] == -1)
+    assert np.all(idx[..., 0] >= 0)
+    last = np.take_along_axis(idx, (C - 1)[..., None], axis=-1)[..., 0]
+    np.testing.assert_array_equal(last, np.broadcast_to(t, last.shape))
+
+
+# ------------------------------------------------------- entry-point paths --
+def test_unfused_path_equals_fused(torch_dev):
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    w = WORKLOADS["t1k"]
+    Q, K, V, W = host_inputs(w, B=2, H=4)
+    cfg = w.config(batch=2, heads=4)
+    q, k, v, wt = to_dev(torch, dev, Q, K, V, W)
+    say("build / predict / route / attend separately, t1k B2 H4")
+    nodes = alhr.alhr_build_tree(cfg, k)
+    bud = alhr.alhr_predict_budget(cfg, q, k, wt)
+    idx, cnt = alhr.alhr_route(cfg, q, k, nodes, bud)
+    O1 = alhr.alhr_sparse_attend(cfg, q, k, v, idx, cnt)
+    idx2, cnt2, O2 = alhr.alhr_route_attend(cfg, q, k, v, nodes, bud)
+    full = alhr.alhr_forward(cfg, q, k, v, wt)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+    assert torch.equal(idx, full["idx"]) and torch.equal(bud, full["budget"])
+    assert torch.equal(nodes[:, :, 1:], full["nodes"][:, :, 1:])
+    assert (O1 - O2).abs().max().item() <= 1e-6
+    assert torch.equal(O2, full["O"])
+    out = {"budget": bud.cpu().numpy(), "count": cnt.cpu().numpy(), "idx": idx.cpu().numpy(),
+           "O": O1.cpu().numpy()}
+    check_pair(w, cfg, Q, K, V, W, out, 1, 3)
+
+
+def test_route_stats_match_oracle_counts(torch_dev):
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    w = WORKLOADS["t1k"]
+    Q, K, V, W = host_inputs(w, B=1, H=2)
+    cfg = w.config(batch=1, heads=2)
+    q, k, wt = to_dev(torch, dev, Q, K, W)
+    say("alhr_route_stats t1k B1 H2")
+    nodes = alhr.alhr_build_tree(cfg, k)
+    bud = alhr.alhr_predict_budget(cfg, q, k, wt)
+    idx, cnt, st = alhr.alhr_route_stats(cfg, q, k, nodes, bud)
+    idx_r, _ = alhr.alhr_route(cfg, q, k, nodes, bud)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_r)
+    st = st.cpu().numpy()
+    ref = oracle.pair_forward(Q[0, 1], K[0, 1], V[0, 1], W=W, scale=cfg.scale, with_stats=True)
+    for t in range(w.T):
+        s = ref["stats"][t]
+        # only left children are loaded; the right child's score is derived
+        assert st[0, 1, t, 0] == s["cover_internal"] + s["child_internal"] // 2
+        assert st[0, 1, t, 1] == s["cover_leaf"] + s["child_leaf"] // 2
+        assert st[0, 1, t, 2] == s["neighbours"] and st[0, 1, t, 3] == s["count"]
+
+
+def test_repeat_runs_are_bit_identical(torch_dev):
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    w = WORKLOADS["t4k"]
+    Q, K, V, W = host_inputs(w, B=1, H=4)
+    cfg = w.config(batch=1, heads=4)
+    q, k, v, wt = to_dev(torch, dev, Q, K, V, W)
+    say("repeat alhr_forward x5, t4k B1 H4")
+    first = alhr.alhr_forward(cfg, q, k, v, wt)
+    for _ in range(4):
+        again = alhr.alhr_forward(cfg, q, k, v, wt)
+        torch.cuda.synchronize()
+        for key in ("budget", "idx", "count", "O"):
+            assert torch.equal(first[key], again[key]), key
+
+
+# ---------------------------------------------------------------- edges ---
+EDGE_CASES = [
+    # name, T, d, window, fixed budget (0 = predictor), max_budget, kind
+    ("T2", 2, 16, 4, 2, 96, "uniform"),
+    ("T4_w1_b1", 4, 16, 1, 1, 96, "uniform"),
+    ("T8_w1", 8, 32, 1, 5, 96, "uniform"),
+    ("window_over_budget", 64, 32, 40, 16, 96, "uniform"),
+    ("budget_128", 512, 16, 4, 128, 128, "uniform"),
+    ("budget_127_w1", 512, 32, 1, 127, 128, "uniform"),
+    ("d128", 256, 128, 4, 37, 96, "uniform"),
+    ("d256", 128, 256, 4, 50, 96, "uniform"),
+    ("d16_predictor", 512, 16, 4, 0, 96, "clustered"),
+    ("d128_predictor", 1024, 128, 4, 0, 96, "clustered"),
+    ("d32_predictor_w2", 2048, 32, 2, 0, 96, "clustered"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
+def test_edge_cases_every_query(torch_dev, case):
+    torch, dev = torch_dev
+    name, T, d, window, fb, mb, kind = case
+    w = Workload(name, 11, 2, 2, T, d, kind, fixed_budget=fb, window=window, max_budget=mb)
+    Q, K, V, W = host_inputs(w)
+    cfg = w.config()
+    out = run_forward(torch, dev, w, Q, K, V, W, cfg=cfg)
+    for b in range(2):
+        for h in range(2):
+            check_nodes(out["nodes"], K, b, h)
+            check_pair(w, cfg, Q, K, V, W, out, b, h)
+
+
+def test_zero_query_and_planted_keys(torch_dev):
+    """All-tie queries (order falls to position) and planted keys, on the GPU."""
+    torch, dev = torch_dev
+    T, d = 512, 64
+    w = Workload("planted", 12, 1, 2, T, d, "uniform", fixed_budget=24)
+    rng = np.random.default_rng(5)
+    Q = np.zeros((1, 2, T, d), np.int8)
+    K = rng.integers(-4, 5, size=(1, 2, T, d)).astype(np.int8)
+    Q[0, 1] = rng.integers(1, 5, size=(T, d))
+    K[0, 1] = 0
+    planted = rng.choice(T, size=40, replace=False)
+    K[0, 1, planted] = rng.integers(1, 5, size=(40, d))
+    V = synth.values(12, 1, 2, d, 0, T)
+    out = run_forward(torch, dev, w, Q, K, V, None)
+    cfg = w.config()
+    for h in range(2):
+        check_pair(w, cfg, Q, K, V, None, out, 0, h)
+    t = T - 1
+    sel = out["idx"][0, 0, t, :24]
+    np.testing.assert_array_equal(sel[:20], np.arange(20))   # ties: lowest positions
+
+
+def test_wide_int32_path(torch_dev):
+    """Bounds that rule out 24-bit multiplies (kmax * T/2 >= 2^23) take the
+    full 32-bit scoring path; same parity bar on sampled queries."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    T, d = 1 << 18, 16
+    rng = np.random.default_rng(6)
+    K = rng.integers(-127, 128, size=(1, 1, T, d)).astype(np.int8)
+    Q = rng.integers(-4, 5, size=(1, 1, T, d)).astype(np.int8)
+    V = synth.values(13, 1, 1, d, 0, T)
+    w = Workload("wide", 13, 1, 1, T, d, "uniform", fixed_budget=40)
+    cfg = w.config(kmax=127, qmax=4)
+    assert cfg.kmax * (T // 2) >= 1 << 23
+    out = run_forward(torch, dev, w, Q, K, V, None, cfg=cfg)
+    check_nodes(out["nodes"], K, 0, 0)
+    ts = sample_ts(T, np.random.default_rng(1), 256)
+    check_pair(w, cfg, Q, K, V, None, out, 0, 0, ts=ts)
+
+
+def test_budget_array_values_are_clamped(torch_dev):
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    w = WORKLOADS["tiny"]
+    Q, K, V, _ = host_inputs(w)
+    cfg = w.config()
+    q, k, v = to_dev(torch, dev, Q, K, V)
+    nodes = alhr.alhr_build_tree(cfg, k)
+    raw = np.full((1, 1, w.T), 7, np.int32)
+    raw[0, 0, ::3] = 0
+    raw[0, 0, 1::3] = 500
+    say("alhr_route with out-of-range budgets (clamped)")
+    idx, cnt = alhr.alhr_route(cfg, q, k, nodes, torch.from_numpy(raw).to(dev))
+    torch.cuda.synchronize()
+    clamped = np.clip(raw, 1, cfg.max_budget)[0, 0]
+    np.testing.assert_array_equal(cnt.cpu().numpy()[0, 0], np.minimum(clamped, np.arange(w.T) + 1))
+
+
+def test_invalid_arguments_rejected_on_device(torch_dev):
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    cfg = alhr.Config(batch=1, heads=1, T=64, d=32)
+    k = torch.zeros((1, 1, 64, 32), dtype=torch.int8, device=dev)
+    nodes = alhr.alhr_build_tree(cfg, k)
+    with pytest.raises(alhr.AlhrError) as e:
+        alhr.alhr_route(cfg, k, k, nodes, None, fixed_budget=0)
+    assert e.value.status == -1
+    bad = alhr.Config(batch=1, heads=1, T=64, d=48)
+    with pytest.raises(alhr.AlhrError) as e:
+        alhr.alhr_build_tree(bad, torch.zeros((1, 1, 64, 48), dtype=torch.int8, device=dev))
+    assert e.value.status == -4
