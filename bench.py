@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the ALHR tree-attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload t16k]
+
+A step is one pass of the whole prefill path over one batch: tree build,
+budget prediction, and the fused route + attend kernel, i.e. the kernels
+alhr_forward launches, issued as the three ABI calls so that HIP events on
+the launch stream can time each kernel.  Inputs are synthetic and resident
+in HBM before the timed region.  Prints one JSON line:
+
+  value     routed queries/s of the whole step (B * H * T queries per step)
+  roofline  the fused route + attend kernel: algorithmic bytes per launch
+            (from the kernel's own per-query load counts) over its average
+            event-timed duration, against 8 TB/s; `traffic` is the rocprofv3
+            FETCH_SIZE + WRITE_SIZE of that kernel (scaled by a plain-copy
+            calibration) when the recorded counters match the current
+            kernel source, else null
+  cpu_baseline  the single-threaded C oracle on a bounded sample of the same
+            workload, timed on this host
+
+The decode workload (--workload decode) times 128-token decode loops on the
+2^17-position, 64 x 16-head cache: append + route + attend per token.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "route_attend_t16k_counters.txt")
+ROUTE_SOURCES = [os.path.join(ROOT, "learned_tree_routed_amd", "csrc", f)
+                 for f in ("route.hip", "device.h")]
+
+
+def route_source_sha():
+    h = hashlib.sha256()
+    for p in ROUTE_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(bytes_unit=1024):
+    """HBM bytes per launch of the route kernel from the committed counter
+    summary, or None when absent or taken on other kernel source."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    kv = {}
+    for line in open(PROFILE_COUNTERS):
+        line = line.split("#")[0].strip()
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("route_source_sha") != route_source_sha():
+        return None
+    try:
+        f = float(kv["fetch_kib_per_dispatch"]) * float(kv["copy_fetch_factor"])
+        w = float(kv["write_kib_per_dispatch"]) * float(kv["copy_write_factor"])
+    except (KeyError, ValueError):
+        return None
+    return (f + w) * bytes_unit
+
+
+def bytes_per_query(stats, cfg, budget_read=True):
+    """Algorithmic bytes of the fused kernel per query from its load counts:
+    q row, neighbour key rows, tree rows loaded (left children and cover
+    roots, int32), key rows loaded by the descent, value rows (fp32), the
+    output row, the idx row and the count (and the budget it reads)."""
+    d = cfg.d
+    tree_rows, key_rows, n, C = (stats[..., i].astype(np.int64) for i in range(4))
+    b = (d + n * d + tree_rows * 4 * d + key_rows * d + C * 4 * d + 4 * d
+         + 4 * cfg.max_budget + 4 + (4 if budget_read else 0))
+    return b
+
+
+def cpu_baseline(w, Q, K, V, W, stride):
+    import oracle
+    import learned_tree_routed_amd as alhr  # noqa: F401  (scale convention)
+    cfg = w.config()
+    ts = np.arange(0, w.T, stride, dtype=np.int32)
+    t0 = time.perf_counter()
+    n = 0
+    for b in range(w.B):
+        for h in range(w.H):
+            oracle.pair_forward(Q[b, h], K[b, h], V[b, h], W=W, fixed_budget=w.fixed_budget,
+                                window=cfg.window, keys_per_class=cfg.keys_per_class,
+                                max_budget=cfg.max_budget, scale=cfg.scale, ts=ts)
+            n += len(ts)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": "%s: every %d-th query of all %d (b, h) pairs (%d queries), each pair "
+                      "with its full tree build and prefix; single-threaded C oracle, %.1f s"
+                      % (w.name, stride, w.B * w.H, n, dt)}
+
+
+def bench_prefill(args, torch, dev):
+    import learned_tree_routed_amd as alhr
+    from synth.workloads import WORKLOADS, host_inputs
+    w = WORKLOADS[args.workload]
+    if args.budget_override:
+        import dataclasses
+        w = dataclasses.replace(w, fixed_budget=args.budget_override)
+    cfg = w.config()
+    Q, K, V, W = host_inputs(w)
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (Q, K, V))
+    wt = None if W is None else torch.from_numpy(W).to(dev)
+    rows = (w.B, w.H, w.T, w.d)
+    nodes = torch.empty(rows, dtype=torch.int32, device=dev)
+    budget = torch.empty((w.B, w.H, w.T), dtype=torch.int32, device=dev)
+    idx = torch.empty((w.B, w.H, w.T, cfg.max_budget), dtype=torch.int32, device=dev)
+    count = torch.empty((w.B, w.H, w.T), dtype=torch.int32, device=dev)
+    O = torch.empty(rows, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(alhr.alhr_workspace_bytes(cfg), 256), dtype=torch.uint8, device=dev)
+    fixed = w.fixed_budget
+
+    def step(ev):
+        ev[0].record()
+        alhr.alhr_build_tree(cfg, k, nodes)
+        ev[1].record()
+        if wt is not None:
+            alhr.alhr_predict_budget(cfg, q, k, wt, budget, ws)
+        ev[2].record()
+        alhr.alhr_route_attend(cfg, q, k, v, nodes, budget if wt is not None else None, fixed,
+                               idx, count, O)
+        ev[3].record()
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(4)]  # noqa: E731
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    events = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern = {name: float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
+            for name, a, b in (("build_ms", 0, 1), ("predict_ms", 1, 2), ("route_attend_ms", 2, 3))}
+
+    # load counts of the routing (untimed), for the byte model
+    _, _, st = alhr.alhr_route_stats(cfg, q, k, nodes, budget if wt is not None else None, fixed)
+    torch.cuda.synchronize()
+    stats = st.cpu().numpy()
+    bpl = int(bytes_per_query(stats, cfg, wt is not None).sum())
+    achieved = bpl / (kern["route_attend_ms"] * 1e-3) / 1e9
+    traffic = read_traffic() if (args.workload == "t16k" and not args.budget_override) else None
+    cnt = count.cpu().numpy()
+    bud = budget.cpu().numpy() if wt is not None else np.full_like(cnt, fixed)
+    queries = w.B * w.H * w.T
+    out = {
+        "metric": "routed queries/sec (build+route+attend) at T=16384; % of HBM peak",
+        "value": queries / (ms_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8/int32 routing, fp32 attention",
+        "data": "synthetic (clustered int8 keys, noisy copied queries, seeded)",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "T": w.T, "d": w.d,
+                   "window": cfg.window, "max_budget": cfg.max_budget,
+                   "budget": ("fixed %d" % fixed) if fixed else "int8 predictor, 32 classes x 3",
+                   "queries_per_step": queries},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "k_route (fused route + attend)",
+                     "bytes_per_launch": bpl, "ms_per_launch": kern["route_attend_ms"]},
+        "kernels_ms": kern,
+        "diagnostics": {"mean_budget": float(bud.mean()), "mean_keys_per_query": float(cnt.mean()),
+                        "mean_tree_rows_loaded": float(stats[..., 0].mean()),
+                        "mean_key_rows_loaded": float(stats[..., 1].mean()),
+                        "bytes_per_query": bpl / queries,
+                        "compression_T_over_keys": float(w.T / cnt.mean()),
+                        "compression_causal_over_keys": float((w.T + 1) / 2 / cnt.mean())},
+    }
+    return out, (w, Q, K, V, W)
+
+
+def bench_decode(args, torch, dev):
+    import learned_tree_routed_amd as alhr
+    from synth import device as sd
+    from synth.workloads import WORKLOADS
+    w = WORKLOADS["decode"]
+    cfg = w.config()
+    B, H, T, d, n0, S = w.B, w.H, w.T, w.d, w.n0, w.steps
+    K = torch.zeros((B, H, T, d), dtype=torch.int8, device=dev)
+    V = torch.zeros((B, H, T, d), dtype=torch.float32, device=dev)
+    nodes = torch.empty((B, H, T, d), dtype=torch.int32, device=dev)
+    sd.keys_(K, w.seed, 0, n0)
+    sd.values_(V, w.seed, 0, n0)
+    Wd = sd.weights_(torch.empty((32, 2 * d), dtype=torch.int8, device=dev), w.seed)
+    kn = sd.keys_(torch.empty((B, H, S, d), dtype=torch.int8, device=dev), w.seed, n0)
+    vn = sd.values_(torch.empty((B, H, S, d), dtype=torch.float32, device=dev), w.seed, n0)
+    qn = sd.queries_(torch.empty((B, H, S, d), dtype=torch.int8, device=dev), w.seed, n0)
+    ks = [kn[:, :, s].contiguous() for s in range(S)]
+    vs = [vn[:, :, s].contiguous() for s in range(S)]
+    qs = [qn[:, :, s].contiguous() for s in range(S)]
+    idx = torch.empty((B, H, cfg.max_budget), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
+    O = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    bud = torch.empty((B, H), dtype=torch.int32, device=dev)
+
+    prefix = torch.empty((B, H, d), dtype=torch.int32, device=dev)
+
+    def reset():
+        # untimed: drop the appended rows and rebuild the cache of n0 keys
+        K[:, :, n0:].zero_()
+        V[:, :, n0:].zero_()
+        alhr.alhr_build_tree(cfg, K, nodes)
+        alhr.alhr_prefix_from_tree(cfg, n0, K, nodes, prefix)
+
+    def loop():
+        for s in range(S):
+            alhr.alhr_append(cfg, n0 + s, ks[s], vs[s], K, V, nodes, prefix)
+            alhr.alhr_decode_step(cfg, n0 + s, qs[s], K, V, nodes, prefix, Wd, 0, bud, idx, cnt, O)
+
+    # eager loop once (also the warm-up), then the same 2 x 128 launches
+    # captured in a HIP graph; each timed replay starts from a reset cache
+    reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loop()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3
+    graph = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        loop()
+    for _ in range(args.warmup):
+        reset()
+        graph.replay()
+    times = []
+    for _ in range(args.steps):
+        reset()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record()
+        graph.replay()
+        ev[1].record()
+        torch.cuda.synchronize()
+        times.append(((time.perf_counter() - t0) * 1e3, ev[0].elapsed_time(ev[1])))
+    ms = float(np.mean([t[0] for t in times]))
+    queries = B * H * S
+    return {
+        "metric": "routed queries/sec (append+route+attend), decode at T=2^17",
+        "value": queries / (ms * 1e-3), "unit": "queries/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8/int32 routing, fp32 attention",
+        "data": "synthetic (device-generated clustered keys, seeded)",
+        "config": {"workload": "decode", "sequences": B, "heads": H, "T": T, "d": d,
+                   "prefilled": n0, "tokens_per_step": S, "queries_per_step": queries,
+                   "launch": "HIP graph of 128 x (append, decode step)"},
+        "diagnostics": {"mean_keys_last_step": float(cnt.float().mean().item()),
+                        "event_ms_per_step": float(np.mean([t[1] for t in times])),
+                        "eager_ms_per_step": eager_ms},
+    }, None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="t16k", choices=["tiny", "t1k", "t4k", "t16k", "decode"])
+    ap.add_argument("--budget-override", type=int, default=0,
+                    help="fixed budget for every query instead of the predictor (context runs)")
+    ap.add_argument("--cpu-stride", type=int, default=2,
+                    help="oracle baseline routes every k-th query of every pair")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB read + 1 GiB write elementwise kernel (x5), the "
+                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU; the ALHR path shards by (batch, head) "
+              "pair with no exchange, and no multi-GPU run is part of it (--gpus %d requested)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = (1 << 30) // 4
+        x = torch.ones(n, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"kernel": "elementwise neg, fp32",
+                                               "read_bytes": 4 * n, "write_bytes": 4 * n,
+                                               "dispatches": 5}}), flush=True)
+        return
+    if args.workload == "decode":
+        out, inputs = bench_decode(args, torch, dev)
+    else:
+        out, inputs = bench_prefill(args, torch, dev)
+    if inputs is not None and not args.no_cpu_baseline:
+        w, Q, K, V, W = inputs
+        out["cpu_baseline"] = cpu_baseline(w, Q, K, V, W, args.cpu_stride)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
