@@ -14,6 +14,7 @@ namespace alhr {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMaxLevels = 20;   // T <= 2^20
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_append(const int8_t* __restrict__ k_new,
@@ -34,15 +35,23 @@ __global__ __launch_bounds__(kThreads) void k_append(const int8_t* __restrict__ 
     reinterpret_cast<int*>(K)[row * C4 + g] = kw;
     reinterpret_cast<float4*>(V)[row * C4 + g] =
         reinterpret_cast<const float4*>(v_new)[(size_t)pair * C4 + g];
+    // all L ancestor cells are loaded before any is stored, so the loads are
+    // in flight together instead of one dependent round trip per level
     int4* tree = reinterpret_cast<int4*>(nodes) + (size_t)pair * T * C4;
-    for (int l = 1; l <= L; ++l) {
-        int4* cell = tree + (size_t)((T >> l) + (pos >> l)) * C4 + g;
-        int4 v = *cell;
-        v.x += kv.x;
-        v.y += kv.y;
-        v.z += kv.z;
-        v.w += kv.w;
-        *cell = v;
+    int4 cells[kMaxLevels];
+#pragma unroll
+    for (int l = 1; l <= kMaxLevels; ++l)
+        if (l <= L) cells[l - 1] = tree[(size_t)((T >> l) + (pos >> l)) * C4 + g];
+#pragma unroll
+    for (int l = 1; l <= kMaxLevels; ++l) {
+        if (l <= L) {
+            int4 v = cells[l - 1];
+            v.x += kv.x;
+            v.y += kv.y;
+            v.z += kv.z;
+            v.w += kv.w;
+            tree[(size_t)((T >> l) + (pos >> l)) * C4 + g] = v;
+        }
     }
     int4* pre = reinterpret_cast<int4*>(prefix) + (size_t)pair * C4 + g;
     int4 p = *pre;

@@ -39,6 +39,80 @@ __device__ __forceinline__ uint32_t mbcnt(uint64_t m)
 
 __device__ __forceinline__ int wave_count(bool p) { return popc64(__ballot(p)); }
 
+// Marks a value that is the same in every lane, so the compiler keeps it in
+// a scalar register and branches on it with scalar code.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t uniform(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+// ---- cross-lane reductions with DPP (no LDS traffic) ----------------------
+// gfx9 DPP controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
+// row_mirror = 0x140, row_half_mirror = 0x141.
+template <int CTRL> __device__ __forceinline__ int dpp(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL> __device__ __forceinline__ float dppf(float v)
+{
+    return __int_as_float(dpp<CTRL>(__float_as_int(v)));
+}
+
+// Sum over aligned groups of G consecutive lanes (G in 1, 2, 4, 8, 16); every
+// lane of the group receives the group sum.
+template <int G> __device__ __forceinline__ int group_sum(int v)
+{
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
+    if constexpr (G >= 2) v += dpp<0xB1>(v);
+    if constexpr (G >= 4) v += dpp<0x4E>(v);
+    if constexpr (G >= 8) v += dpp<0x141>(v);
+    if constexpr (G >= 16) v += dpp<0x140>(v);
+    return v;
+}
+
+// Whole-wave reductions returning a wave-uniform value: butterfly within each
+// 16-lane row by DPP, then the four row results combined with readlane.
+template <typename Op> __device__ __forceinline__ int wave_reduce_i(int v, Op op)
+{
+    v = op(v, dpp<0xB1>(v));
+    v = op(v, dpp<0x4E>(v));
+    v = op(v, dpp<0x141>(v));
+    v = op(v, dpp<0x140>(v));
+    const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return uniform(op(op(a, b), op(c, d)));
+}
+template <typename Op> __device__ __forceinline__ float wave_reduce_f(float v, Op op)
+{
+    v = op(v, dppf<0xB1>(v));
+    v = op(v, dppf<0x4E>(v));
+    v = op(v, dppf<0x141>(v));
+    v = op(v, dppf<0x140>(v));
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return op(op(a, b), op(c, d));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    return (uint32_t)wave_reduce_i((int)v, [](int a, int b) { return (int)((uint32_t)a > (uint32_t)b ? a : b); });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+    return (uint32_t)wave_reduce_i((int)v, [](int a, int b) { return (int)((uint32_t)a < (uint32_t)b ? a : b); });
+}
+__device__ __forceinline__ float wave_max_f(float v)
+{
+    return wave_reduce_f(v, [](float a, float b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ float wave_sum_f(float v)
+{
+    return wave_reduce_f(v, [](float a, float b) { return a + b; });
+}
+
+// Generic shuffle reduction, for the rare wider types.
 template <typename T> __device__ __forceinline__ T wave_max(T v)
 {
 #pragma unroll
@@ -46,32 +120,6 @@ template <typename T> __device__ __forceinline__ T wave_max(T v)
         T w = __shfl_xor(v, o);
         v = w > v ? w : v;
     }
-    return v;
-}
-
-template <typename T> __device__ __forceinline__ T wave_min(T v)
-{
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        T w = __shfl_xor(v, o);
-        v = w < v ? w : v;
-    }
-    return v;
-}
-
-template <typename T> __device__ __forceinline__ T wave_sum(T v)
-{
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
-// Sum over aligned groups of G consecutive lanes (G a power of two <= 64);
-// every lane of the group receives the group sum.
-template <int G, typename T> __device__ __forceinline__ T group_sum(T v)
-{
-#pragma unroll
-    for (int o = 1; o < G; o <<= 1) v += __shfl_xor(v, o);
     return v;
 }
 

@@ -123,64 +123,67 @@ __device__ __forceinline__ int score_node(const int32_t* __restrict__ nodes_pair
 }
 
 // Keep the best min(r, #non-empty) keys of cand[0, n) (0 = empty slot) in
-// beam[0, ...); returns how many were kept.  The order of beam is the slot
-// order of the winners (the set is what matters: keys are distinct).
-__device__ int select_best(const uint64_t* cand, int n, int r, uint64_t* beam)
+// beam[0, ...), in slot order, and return how many were kept; `inner` tells
+// whether any kept node is internal.  NS slots per lane (n <= 64 * NS).
+template <int NS>
+__device__ int select_best_ns(const uint64_t* cand, int n, int r, uint64_t* beam, bool& inner)
 {
     const int lane = lane_id();
-    uint64_t k[4];
+    uint64_t k[NS];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NS; ++j) {
         const int sl = lane + kWave * j;
-        k[j] = (kWave * j < n && sl < n) ? cand[sl] : 0ull;
+        k[j] = sl < n ? cand[sl] : 0ull;
     }
     int nvalid = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) nvalid += wave_count(k[j] != 0ull);
-    bool sel[4];
+    for (int j = 0; j < NS; ++j) nvalid += wave_count(k[j] != 0ull);
+    bool sel[NS];
     if (nvalid <= r) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sel[j] = k[j] != 0ull;
+        for (int j = 0; j < NS; ++j) sel[j] = k[j] != 0ull;
     } else {
-        uint32_t h[4];
+        uint32_t h[NS];
         uint32_t mx = 0u, mn = 0xFFFFFFFFu;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NS; ++j) {
             h[j] = (uint32_t)(k[j] >> 32);   // empty slots: 0, below every real key
             if (k[j] != 0ull) {
                 mx = h[j] > mx ? h[j] : mx;
                 mn = h[j] < mn ? h[j] : mn;
             }
         }
-        mx = wave_max(mx);
-        mn = wave_min(mn);
-        // largest threshold with at least r scores >= it
-        uint32_t lo = mn, hb = mx;
+        mx = wave_max_u32(mx);
+        mn = wave_min_u32(mn);
+        // largest threshold with at least r scores >= it (scalar loop)
+        uint32_t lo = uniform(mn), hb = uniform(mx);
         while (lo < hb) {
             const uint32_t mid = lo + ((hb - lo + 1u) >> 1);
             int c = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) c += wave_count(h[j] >= mid);
+            for (int j = 0; j < NS; ++j) c += wave_count(h[j] >= mid);
             if (c >= r) lo = mid;
             else hb = mid - 1u;
+            lo = uniform(lo);
+            hb = uniform(hb);
         }
         int gt = 0, eq = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NS; ++j) {
             gt += wave_count(h[j] > lo);
             eq += wave_count(k[j] != 0ull && h[j] == lo);
         }
         const int need = r - gt;
         if (need == eq) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sel[j] = k[j] != 0ull && h[j] >= lo;
+            for (int j = 0; j < NS; ++j) sel[j] = k[j] != 0ull && h[j] >= lo;
         } else {
             // ties at the threshold: keep the `need` lowest starts (largest low words)
-            bool tie[4];
-            uint32_t l[4];
+            bool tie[NS];
+            uint32_t l[NS];
             uint32_t lmx = 0u, lmn = 0xFFFFFFFFu;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NS; ++j) {
                 tie[j] = k[j] != 0ull && h[j] == lo;
                 l[j] = (uint32_t)k[j];
                 if (tie[j]) {
@@ -188,30 +191,44 @@ __device__ int select_best(const uint64_t* cand, int n, int r, uint64_t* beam)
                     lmn = l[j] < lmn ? l[j] : lmn;
                 }
             }
-            lmx = wave_max(lmx);
-            lmn = wave_min(lmn);
-            uint32_t a = lmn, b = lmx;
-            while (a < b) {
-                const uint32_t mid = a + ((b - a + 1u) >> 1);
+            lmx = wave_max_u32(lmx);
+            lmn = wave_min_u32(lmn);
+            uint32_t a = uniform(lmn), bb = uniform(lmx);
+            while (a < bb) {
+                const uint32_t mid = a + ((bb - a + 1u) >> 1);
                 int c = 0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) c += wave_count(tie[j] && l[j] >= mid);
+                for (int j = 0; j < NS; ++j) c += wave_count(tie[j] && l[j] >= mid);
                 if (c >= need) a = mid;
-                else b = mid - 1u;
+                else bb = mid - 1u;
+                a = uniform(a);
+                bb = uniform(bb);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NS; ++j)
                 sel[j] = (k[j] != 0ull && h[j] > lo) || (tie[j] && l[j] >= a);
         }
     }
     int base = 0;
+    bool any_inner = false;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NS; ++j) {
         const uint64_t msk = __ballot(sel[j]);
         if (sel[j]) beam[base + (int)mbcnt(msk)] = k[j];
         base += popc64(msk);
+        any_inner |= __ballot(sel[j] && key_level(k[j]) > 0) != 0ull;
     }
+    inner = any_inner;
     return base;
+}
+
+__device__ __forceinline__ int select_best(const uint64_t* cand, int n, int r, uint64_t* beam,
+                                           bool& inner)
+{
+    if (n <= kWave) return select_best_ns<1>(cand, n, r, beam, inner);
+    if (n <= 2 * kWave) return select_best_ns<2>(cand, n, r, beam, inner);
+    if (n <= 3 * kWave) return select_best_ns<3>(cand, n, r, beam, inner);
+    return select_best_ns<4>(cand, n, r, beam, inner);
 }
 
 struct RouteCounts {
@@ -229,8 +246,8 @@ __device__ int route_query(const int32_t* __restrict__ nodes_pair,
     constexpr int LPR = D / 16, RPG = kWave / LPR;
     const int lane = lane_id();
     const int s = lane % LPR, g = lane / LPR;
-    const int C = B < t + 1 ? B : t + 1;
-    const int n = window < C ? window : C;
+    const int C = uniform(B < t + 1 ? B : t + 1);
+    const int n = uniform(window < C ? window : C);
     const int r = C - n;
     const int m = t + 1 - n;
 
@@ -249,7 +266,10 @@ __device__ int route_query(const int32_t* __restrict__ nodes_pair,
         return C;
     }
 
-    // cover of [0, m): bit l of m set -> node (l, start = m with bits <= l cleared)
+    // cover of [0, m): bit b of m set -> node (b, start = m with bits <= b
+    // cleared).  Slot L-1-b puts the cover in ascending start order; children
+    // of beam entry i go to slots 2i and 2i+1 and the selection compacts in
+    // slot order, so the beam stays sorted by start in every round.
     for (int base = 0; base < L; base += RPG) {
         const int b = base + g;
         const bool act = b < L && ((m >> b) & 1);
@@ -259,16 +279,14 @@ __device__ int route_query(const int32_t* __restrict__ nodes_pair,
             cnt.tree_rows += wave_count(act && s == 0 && b > 0);
             cnt.key_rows += wave_count(act && s == 0 && b == 0);
         }
-        if (b < L && s == 0) sm.cand[b] = act ? make_key(sc, start, b) : 0ull;
+        if (b < L && s == 0) sm.cand[L - 1 - b] = act ? make_key(sc, start, b) : 0ull;
     }
     wave_sync();
-    int nb = select_best(sm.cand, L, r, sm.beam);
+    bool inner;
+    int nb = select_best(sm.cand, L, r, sm.beam, inner);
     wave_sync();
 
-    for (;;) {
-        bool inner = false;
-        for (int i = lane; i < nb; i += kWave) inner |= key_level(sm.beam[i]) > 0;
-        if (!__ballot(inner)) break;
+    while (inner) {
         for (int base = 0; base < nb; base += RPG) {
             const int i = base + g;
             const uint64_t key = i < nb ? sm.beam[i] : 0ull;
@@ -291,29 +309,15 @@ __device__ int route_query(const int32_t* __restrict__ nodes_pair,
             }
         }
         wave_sync();
-        nb = select_best(sm.cand, 2 * nb, r, sm.beam);
+        nb = select_best(sm.cand, 2 * nb, r, sm.beam, inner);
         wave_sync();
     }
 
-    // the r routed keys, in ascending position order, by counting ranks
-    {
-        const uint64_t k0 = lane < r ? sm.beam[lane] : 0ull;
-        const uint64_t k1 = lane + kWave < r ? sm.beam[lane + kWave] : 0ull;
-        const int s0 = key_start(k0), s1 = key_start(k1);
-        int r0 = 0, r1 = 0;
-        for (int j = 0; j < r; ++j) {
-            const int sj = key_start(sm.beam[j]);
-            r0 += sj < s0;
-            r1 += sj < s1;
-        }
-        if (lane < r) {
-            sm.pos[r0] = s0;
-            sm.score[r0] = key_score(k0);
-        }
-        if (lane + kWave < r) {
-            sm.pos[r1] = s1;
-            sm.score[r1] = key_score(k1);
-        }
+    // the r routed keys, already in ascending position order
+    for (int i = lane; i < r; i += kWave) {
+        const uint64_t k = sm.beam[i];
+        sm.pos[i] = key_start(k);
+        sm.score[i] = key_score(k);
     }
     wave_sync();
     return C;
@@ -341,12 +345,12 @@ __device__ void attend_selected(WaveLds& sm, int C, int T, float scale,
     const bool ok1 = lane + kWave < C && (unsigned)sm.pos[lane + kWave] < (unsigned)T;
     const float a0 = ok0 ? (float)sm.score[lane] * scale : -INFINITY;
     const float a1 = ok1 ? (float)sm.score[lane + kWave] * scale : -INFINITY;
-    const float mx = wave_max(a0 > a1 ? a0 : a1);
+    const float mx = wave_max_f(a0 > a1 ? a0 : a1);
     const float e0 = ok0 ? __expf(a0 - mx) : 0.0f;
     const float e1 = ok1 ? __expf(a1 - mx) : 0.0f;
     if (lane < C) sm.w[lane] = e0;
     if (lane + kWave < C) sm.w[lane + kWave] = e1;
-    const float z = wave_sum(e0 + e1);
+    const float z = wave_sum_f(e0 + e1);
     wave_sync();
     const int cv = lane % LPV, rv = lane / LPV;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -383,17 +387,17 @@ __global__ __launch_bounds__(kThreads) void k_route(
     int32_t* __restrict__ stats, int P, int T, int L, int window, int max_budget, float scale)
 {
     __shared__ WaveLds smem[kWavesPerBlock];
-    const int wid = threadIdx.x / kWave;
+    const int wid = uniform((int)(threadIdx.x / kWave));
     const uint64_t gw = (uint64_t)xcd_logical_block() * kWavesPerBlock + wid;
     if (gw >= (uint64_t)P * T) return;
-    const int pair = (int)(gw / (uint64_t)T);
-    const int t = T - 1 - (int)(gw % (uint64_t)T);
+    const int pair = uniform((int)(gw / (uint64_t)T));
+    const int t = uniform(T - 1 - (int)(gw % (uint64_t)T));
     const size_t qrow = (size_t)pair * T + t;
     const int s = lane_id() % (D / 16);
     QueryRegs<D> q;
     load_query<D>(Q + qrow * D, s, q);
     // budgets outside [1, max_budget] are clamped: the beam and idx rows hold max_budget
-    int B = budget ? budget[qrow] : fixed_budget;
+    int B = uniform(budget ? budget[qrow] : fixed_budget);
     B = B < 1 ? 1 : (B > max_budget ? max_budget : B);
     WaveLds& sm = smem[wid];
     RouteCounts cnt{0, 0};
@@ -482,33 +486,191 @@ __device__ __forceinline__ int predict_one(const int8_t* __restrict__ q,
     return b < cap ? b : cap;
 }
 
+// Decode has one query per (sequence, head) and step, so the grid is small
+// and each query's ~log2(T) dependent rounds decide the latency.  A workgroup
+// of kDecodeWaves waves serves one query: every wave scores a share of a
+// round's rows (one pass covers 8 x 64 / (d/16) rows), wave 0 selects between
+// two barriers, and all waves share the value gather.
+constexpr int kDecodeWaves = 8;
+
+struct BlockShared {
+    WaveLds sm;
+    float4 red[kDecodeWaves][kWave];   // per-wave partial output rows
+    int nb, inner, budget;
+    float z;
+};
+
 template <int D, bool MUL24>
-__global__ __launch_bounds__(kThreads) void k_decode(
+__device__ int route_query_block(const int32_t* __restrict__ nodes_pair,
+                                 const int8_t* __restrict__ keys_pair, int T, int L, int t, int B,
+                                 int window, const QueryRegs<D>& q, BlockShared& bs)
+{
+    constexpr int LPR = D / 16, RPG = kWave / LPR, RPB = RPG * kDecodeWaves;
+    WaveLds& sm = bs.sm;
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    const int s = lane % LPR, e0 = wv * RPG + lane / LPR;
+    const int C = uniform(B < t + 1 ? B : t + 1);
+    const int n = uniform(window < C ? window : C);
+    const int r = C - n;
+    const int m = t + 1 - n;
+    RouteCounts unused{0, 0};
+    (void)unused;
+
+    for (int base = 0; base < n; base += RPB) {
+        const int k = base + e0;
+        const bool act = k < n;
+        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, 0, m + k, act, s, q);
+        if (act && s == 0) {
+            sm.pos[r + k] = m + k;
+            sm.score[r + k] = sc;
+        }
+    }
+    if (r == 0) {
+        __syncthreads();
+        return C;
+    }
+    for (int base = 0; base < L; base += RPB) {
+        const int b = base + e0;
+        const bool act = b < L && ((m >> b) & 1);
+        const int start = act ? (m & ~((2 << b) - 1)) : 0;
+        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, b, start, act, s, q);
+        if (b < L && s == 0) sm.cand[L - 1 - b] = act ? make_key(sc, start, b) : 0ull;
+    }
+    __syncthreads();
+    int ncand = L;
+    for (;;) {
+        if (wv == 0) {
+            wave_sync();
+            bool inner;
+            const int nb = select_best(sm.cand, ncand, r, sm.beam, inner);
+            if (lane == 0) {
+                bs.nb = nb;
+                bs.inner = inner;
+            }
+        }
+        __syncthreads();
+        const int nb = uniform(bs.nb);
+        if (!uniform(bs.inner)) break;
+        for (int base = 0; base < nb; base += RPB) {
+            const int i = base + e0;
+            const uint64_t key = i < nb ? sm.beam[i] : 0ull;
+            const int lv = key_level(key), st = key_start(key);
+            const bool expand = i < nb && lv > 0;
+            const int cl = lv - 1;
+            const int left = score_node<D, MUL24>(nodes_pair, keys_pair, T, cl, st, expand, s, q);
+            if (i < nb && s == 0) {
+                if (expand) {
+                    sm.cand[2 * i] = make_key(left, st, cl);
+                    sm.cand[2 * i + 1] = make_key(key_score(key) - left, st + (1 << cl), cl);
+                } else {
+                    sm.cand[2 * i] = key;
+                    sm.cand[2 * i + 1] = 0ull;
+                }
+            }
+        }
+        ncand = 2 * nb;
+        __syncthreads();
+    }
+    // the beam is in ascending position order
+    for (int i = threadIdx.x; i < r; i += kDecodeWaves * kWave) {
+        const uint64_t k = sm.beam[i];
+        sm.pos[i] = key_start(k);
+        sm.score[i] = key_score(k);
+    }
+    __syncthreads();
+    return C;
+}
+
+// Softmax weights by wave 0, the value gather shared by every wave, partial
+// rows summed through LDS.
+template <int D>
+__device__ void attend_block(BlockShared& bs, int C, int T, float scale,
+                             const float* __restrict__ values_pair, float* __restrict__ out)
+{
+    constexpr int LPV = D / 4, RPV = kWave / LPV, RPB = RPV * kDecodeWaves;
+    WaveLds& sm = bs.sm;
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    if (wv == 0) {
+        const bool ok0 = lane < C && (unsigned)sm.pos[lane] < (unsigned)T;
+        const bool ok1 = lane + kWave < C && (unsigned)sm.pos[lane + kWave] < (unsigned)T;
+        const float a0 = ok0 ? (float)sm.score[lane] * scale : -INFINITY;
+        const float a1 = ok1 ? (float)sm.score[lane + kWave] * scale : -INFINITY;
+        const float mx = wave_max_f(a0 > a1 ? a0 : a1);
+        const float e0 = ok0 ? __expf(a0 - mx) : 0.0f;
+        const float e1 = ok1 ? __expf(a1 - mx) : 0.0f;
+        if (lane < C) sm.w[lane] = e0;
+        if (lane + kWave < C) sm.w[lane + kWave] = e1;
+        const float z = wave_sum_f(e0 + e1);
+        if (lane == 0) bs.z = z;
+    }
+    __syncthreads();
+    const int cv = lane % LPV, rv = lane / LPV;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = wv * RPV + rv; c < C; c += RPB) {
+        const int j = sm.pos[c];
+        if ((unsigned)j >= (unsigned)T) continue;
+        const float wt = sm.w[c];
+        const float4 v = reinterpret_cast<const float4*>(values_pair + (size_t)j * D)[cv];
+        acc.x += wt * v.x;
+        acc.y += wt * v.y;
+        acc.z += wt * v.z;
+        acc.w += wt * v.w;
+    }
+#pragma unroll
+    for (int o = LPV; o < kWave; o <<= 1) {
+        acc.x += __shfl_xor(acc.x, o);
+        acc.y += __shfl_xor(acc.y, o);
+        acc.z += __shfl_xor(acc.z, o);
+        acc.w += __shfl_xor(acc.w, o);
+    }
+    if (rv == 0) bs.red[wv][cv] = acc;
+    __syncthreads();
+    if (wv == 0 && lane < LPV) {
+        float4 t = bs.red[0][lane];
+#pragma unroll
+        for (int w = 1; w < kDecodeWaves; ++w) {
+            const float4 u = bs.red[w][lane];
+            t.x += u.x;
+            t.y += u.y;
+            t.z += u.z;
+            t.w += u.w;
+        }
+        const float inv = bs.z > 0.0f ? 1.0f / bs.z : 0.0f;
+        reinterpret_cast<float4*>(out)[lane] = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+    }
+}
+
+template <int D, bool MUL24>
+__global__ __launch_bounds__(kDecodeWaves * kWave) void k_decode(
     const int8_t* __restrict__ q_new, const int8_t* __restrict__ K, const float* __restrict__ V,
     const int32_t* __restrict__ nodes, const int32_t* __restrict__ prefix,
     const int8_t* __restrict__ W, int fixed_budget, int32_t* __restrict__ budget_out,
     int32_t* __restrict__ idx, int32_t* __restrict__ count, float* __restrict__ O, int P, int T,
     int L, int pos, int window, int nc, int kpc, int max_budget, float scale)
 {
-    __shared__ WaveLds smem[kWavesPerBlock];
-    const int wid = threadIdx.x / kWave;
-    const uint64_t gw = (uint64_t)xcd_logical_block() * kWavesPerBlock + wid;
-    if (gw >= (uint64_t)P) return;
-    const int pair = (int)gw;
-    const int s = lane_id() % (D / 16);
+    __shared__ BlockShared bs;
+    const uint32_t pair = xcd_logical_block();
+    if (pair >= (uint32_t)P) return;   // uniform over the workgroup
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    const int s = lane % (D / 16);
     const int8_t* qp = q_new + (size_t)pair * D;
     QueryRegs<D> q;
     load_query<D>(qp, s, q);
-    const int B = W ? predict_one<D>(qp, prefix + (size_t)pair * D, W, nc, kpc, max_budget)
-                    : fixed_budget;
-    if (budget_out && lane_id() == 0) budget_out[pair] = B;
-    WaveLds& sm = smem[wid];
-    RouteCounts cnt{0, 0};
-    const int C = route_query<D, MUL24, false>(nodes + (size_t)pair * T * D,
-                                                K + (size_t)pair * T * D, T, L, pos, B, window,
-                                                q, sm, cnt);
-    write_selection(sm, C, max_budget, idx + (size_t)pair * max_budget, count + pair);
-    attend_selected<D>(sm, C, T, scale, V + (size_t)pair * T * D, O + (size_t)pair * D);
+    if (wv == 0) {
+        const int B = W ? predict_one<D>(qp, prefix + (size_t)pair * D, W, nc, kpc, max_budget)
+                        : fixed_budget;
+        if (lane == 0) {
+            bs.budget = B;
+            if (budget_out) budget_out[pair] = B;
+        }
+    }
+    __syncthreads();
+    const int B = uniform(bs.budget);
+    const int C = route_query_block<D, MUL24>(nodes + (size_t)pair * T * D,
+                                               K + (size_t)pair * T * D, T, L, pos, B, window, q,
+                                               bs);
+    if (wv == 0) write_selection(bs.sm, C, max_budget, idx + (size_t)pair * max_budget, count + pair);
+    attend_block<D>(bs, C, T, scale, V + (size_t)pair * T * D, O + (size_t)pair * D);
 }
 
 unsigned grid_for_waves(uint64_t waves)
@@ -556,13 +718,13 @@ hipError_t decode_d(const Shape& s, int pos, const int8_t* q_new, const int8_t* 
                     int fixed_budget, int32_t* budget, int32_t* idx, int32_t* count, float* O,
                     hipStream_t st)
 {
-    const dim3 grid(grid_for_waves((uint64_t)s.P));
+    const dim3 grid((unsigned)((s.P + kXcds - 1) / kXcds * kXcds));
     if (s.mul24)
-        hipLaunchKernelGGL((k_decode<D, true>), grid, dim3(kThreads), 0, st, q_new, K, V, nodes,
+        hipLaunchKernelGGL((k_decode<D, true>), grid, dim3(kDecodeWaves * kWave), 0, st, q_new, K, V, nodes,
                            prefix, W, fixed_budget, budget, idx, count, O, s.P, s.T, s.L, pos,
                            s.window, s.n_classes, s.keys_per_class, s.max_budget, s.scale);
     else
-        hipLaunchKernelGGL((k_decode<D, false>), grid, dim3(kThreads), 0, st, q_new, K, V, nodes,
+        hipLaunchKernelGGL((k_decode<D, false>), grid, dim3(kDecodeWaves * kWave), 0, st, q_new, K, V, nodes,
                            prefix, W, fixed_budget, budget, idx, count, O, s.P, s.T, s.L, pos,
                            s.window, s.n_classes, s.keys_per_class, s.max_budget, s.scale);
     return hipGetLastError();
