@@ -269,6 +269,115 @@ def bench_decode(args, torch, dev):
     }, None
 
 
+def bench_sweep(args, torch, dev):
+    """Length sweep (T = 2^10 .. 2^17, B1 H8 d64, predictor): time per step and
+    per fused launch, the per-query load counts, the device footprint, and a
+    least-squares exponent of time vs T."""
+    import learned_tree_routed_amd as alhr
+    from synth import device as sd
+    from synth.workloads import Workload
+    lines, Ts, ms_all = [], [], []
+    for L in range(10, 18):
+        T = 1 << L
+        w = Workload("sweep", 4, 1, 8, T, 64, "clustered")
+        cfg = w.config()
+        shape = (w.B, w.H, T, w.d)
+        K = sd.keys_(torch.empty(shape, dtype=torch.int8, device=dev), w.seed)
+        Q = sd.queries_(torch.empty(shape, dtype=torch.int8, device=dev), w.seed)
+        V = sd.values_(torch.empty(shape, dtype=torch.float32, device=dev), w.seed)
+        Wt = sd.weights_(torch.empty((32, 128), dtype=torch.int8, device=dev), w.seed)
+        nodes = torch.empty(shape, dtype=torch.int32, device=dev)
+        bud = torch.empty((1, 8, T), dtype=torch.int32, device=dev)
+        idx = torch.empty((1, 8, T, cfg.max_budget), dtype=torch.int32, device=dev)
+        cnt = torch.empty((1, 8, T), dtype=torch.int32, device=dev)
+        O = torch.empty(shape, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(alhr.alhr_workspace_bytes(cfg), 256), dtype=torch.uint8, device=dev)
+
+        def step(ev):
+            ev[0].record()
+            alhr.alhr_build_tree(cfg, K, nodes)
+            alhr.alhr_predict_budget(cfg, Q, K, Wt, bud, ws)
+            ev[1].record()
+            alhr.alhr_route_attend(cfg, Q, K, V, nodes, bud, 0, idx, cnt, O)
+            ev[2].record()
+        for _ in range(2):
+            step([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e in evs:
+            step(e)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        kms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        _, _, st = alhr.alhr_route_stats(cfg, Q, K, nodes, bud, 0)
+        stats = st.cpu().numpy()
+        bpl = int(bytes_per_query(stats, cfg).sum())
+        state = K.numel() + 4 * V.numel() + 4 * nodes.numel()
+        q = w.B * w.H * T
+        lines.append({"sweep_T": T, "queries": q, "ms_per_step": ms, "route_attend_ms": kms,
+                      "routed_qps": q / (ms * 1e-3),
+                      "route_attend_GBps": bpl / (kms * 1e-3) / 1e9,
+                      "mean_keys": float(cnt.float().mean().item()),
+                      "mean_tree_rows": float(stats[..., 0].mean()),
+                      "cache_bytes_K_V_tree": state})
+        Ts.append(T)
+        ms_all.append(ms)
+        del K, Q, V, nodes, idx, O
+        torch.cuda.empty_cache()
+    x = np.log(np.array(Ts, dtype=np.float64))
+    y = np.log(np.array(ms_all))
+    alpha = float(np.polyfit(x, y, 1)[0])
+    per_q = np.array(ms_all) / np.array(Ts)
+    beta = float(np.polyfit(np.log2(np.array(Ts, dtype=np.float64)), per_q / per_q[0], 1)[0])
+    return lines, {"sweep_fit": {"exponent_time_vs_T": alpha,
+                                 "per_query_time_growth_per_doubling": beta,
+                                 "T_range": [Ts[0], Ts[-1]]}}
+
+
+def bench_quality(args, torch, dev):
+    """Routing quality on the synthetic recall task: how often the selected
+    set holds the key the query was copied from, and how much of the dense
+    top-16 (by q . k, the label the README's phase 2 distils) it holds."""
+    import dataclasses
+    import learned_tree_routed_amd as alhr
+    import synth
+    from synth.workloads import WORKLOADS, host_inputs
+    out = []
+    rng = np.random.default_rng(0)
+    for name in ("t1k", "t16k"):
+        base = WORKLOADS[name]
+        Q, K, V, W = host_inputs(base)
+        q, k = (torch.from_numpy(x).to(dev) for x in (Q, K))
+        src = synth.query_sources(base.seed, base.B, base.H, 0, base.T)
+        cfg = base.config()
+        nodes = alhr.alhr_build_tree(cfg, k)
+        wt = torch.from_numpy(W).to(dev)
+        pred = alhr.alhr_predict_budget(cfg, q, k, wt)
+        samples = [(int(rng.integers(base.B)), int(rng.integers(base.H)),
+                    int(rng.integers(64, base.T))) for _ in range(256)]
+        top16 = {}
+        for (b, h, t) in samples:
+            sc = K[b, h, :t + 1].astype(np.int64) @ Q[b, h, t].astype(np.int64)
+            order = np.lexsort((np.arange(t + 1), -sc))
+            top16[(b, h, t)] = set(order[:16].tolist())
+        for budget in (8, 16, 30, 48, 64, 96, 0):
+            bud = pred if budget == 0 else None
+            idx, cnt = alhr.alhr_route(cfg, q, k, nodes, bud, budget)
+            I = idx.cpu().numpy()
+            C = cnt.cpu().numpy()
+            t = np.arange(base.T)
+            hit = (I == src[..., None]).any(axis=-1)[..., 1:]
+            d16 = np.mean([len(top16[x] & set(I[x][:C[x]].tolist())) / 16 for x in samples])
+            out.append({"quality_workload": name, "budget": budget or "predictor",
+                        "mean_keys": float(C.mean()),
+                        "source_key_recall": float(hit.mean()),
+                        "dense_top16_recall_sampled": float(d16),
+                        "window_only_source_recall": float(
+                            ((t[None, None, 1:] - src[..., 1:]) < cfg.window).mean())})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +389,10 @@ def main():
     ap.add_argument("--cpu-stride", type=int, default=2,
                     help="oracle baseline routes every k-th query of every pair")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="length sweep T = 2^10..2^17 with an exponent fit (JSON line per T)")
+    ap.add_argument("--quality", action="store_true",
+                    help="routing-quality diagnostics: source-key and dense top-16 recall")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB read + 1 GiB write elementwise kernel (x5), the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -305,6 +418,16 @@ def main():
         print(json.dumps({"copy_calibration": {"kernel": "elementwise neg, fp32",
                                                "read_bytes": 4 * n, "write_bytes": 4 * n,
                                                "dispatches": 5}}), flush=True)
+        return
+    if args.sweep:
+        lines, fit = bench_sweep(args, torch, dev)
+        for line in lines:
+            print(json.dumps(line), flush=True)
+        print(json.dumps(fit), flush=True)
+        return
+    if args.quality:
+        for line in bench_quality(args, torch, dev):
+            print(json.dumps(line), flush=True)
         return
     if args.workload == "decode":
         out, inputs = bench_decode(args, torch, dev)
