@@ -148,6 +148,20 @@ def bench_prefill(args, torch, dev):
     kern = {name: float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
             for name, a, b in (("build_ms", 0, 1), ("predict_ms", 1, 2), ("route_attend_ms", 2, 3))}
 
+    # the dense causal baseline on the same inputs (MFMA kernel), for the ratio
+    dense_ms = None
+    if w.d >= 32:
+        Od = torch.empty_like(O)
+        alhr.alhr_dense_attend(cfg, q, k, v, Od)
+        dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+        for e in dev_ev:
+            e[0].record()
+            alhr.alhr_dense_attend(cfg, q, k, v, Od)
+            e[1].record()
+        torch.cuda.synchronize()
+        dense_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev]))
+        del Od
+
     # load counts of the routing (untimed), for the byte model
     _, _, st = alhr.alhr_route_stats(cfg, q, k, nodes, budget if wt is not None else None, fixed)
     torch.cuda.synchronize()
@@ -176,6 +190,9 @@ def bench_prefill(args, torch, dev):
                      "kernel": "k_route (fused route + attend)",
                      "bytes_per_launch": bpl, "ms_per_launch": kern["route_attend_ms"]},
         "kernels_ms": kern,
+        "dense_baseline": None if dense_ms is None else {
+            "kernel": "alhr_dense_attend (causal, int8 MFMA scores, fp32 MFMA values)",
+            "ms": dense_ms, "routed_step_speedup": dense_ms / ms_step},
         "diagnostics": {"mean_budget": float(bud.mean()), "mean_keys_per_query": float(cnt.mean()),
                         "mean_tree_rows_loaded": float(stats[..., 0].mean()),
                         "mean_key_rows_loaded": float(stats[..., 1].mean()),
@@ -314,13 +331,22 @@ def bench_sweep(args, torch, dev):
         stats = st.cpu().numpy()
         bpl = int(bytes_per_query(stats, cfg).sum())
         state = K.numel() + 4 * V.numel() + 4 * nodes.numel()
+        alhr.alhr_dense_attend(cfg, Q, K, V, O)
+        de = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)]
+        for e in de:
+            e[0].record()
+            alhr.alhr_dense_attend(cfg, Q, K, V, O)
+            e[1].record()
+        torch.cuda.synchronize()
+        dense_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in de]))
         q = w.B * w.H * T
         lines.append({"sweep_T": T, "queries": q, "ms_per_step": ms, "route_attend_ms": kms,
                       "routed_qps": q / (ms * 1e-3),
                       "route_attend_GBps": bpl / (kms * 1e-3) / 1e9,
                       "mean_keys": float(cnt.float().mean().item()),
                       "mean_tree_rows": float(stats[..., 0].mean()),
-                      "cache_bytes_K_V_tree": state})
+                      "cache_bytes_K_V_tree": state,
+                      "dense_ms": dense_ms, "dense_over_routed_step": dense_ms / ms})
         Ts.append(T)
         ms_all.append(ms)
         del K, Q, V, nodes, idx, O
@@ -328,9 +354,11 @@ def bench_sweep(args, torch, dev):
     x = np.log(np.array(Ts, dtype=np.float64))
     y = np.log(np.array(ms_all))
     alpha = float(np.polyfit(x, y, 1)[0])
+    alpha_dense = float(np.polyfit(x, np.log(np.array([l["dense_ms"] for l in lines])), 1)[0])
     per_q = np.array(ms_all) / np.array(Ts)
     beta = float(np.polyfit(np.log2(np.array(Ts, dtype=np.float64)), per_q / per_q[0], 1)[0])
     return lines, {"sweep_fit": {"exponent_time_vs_T": alpha,
+                                 "exponent_dense_time_vs_T": alpha_dense,
                                  "per_query_time_growth_per_doubling": beta,
                                  "T_range": [Ts[0], Ts[-1]]}}
 

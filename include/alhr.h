@@ -194,6 +194,17 @@ alhr_status alhr_decode_step(const alhr_config *cfg, int32_t pos,
                              int32_t *idx, int32_t *count, float *O,
                              void *stream);
 
+/* Dense causal softmax attention over every past key, the baseline the
+ * README's result tables compare against (dense teacher rows) and the
+ * optimised dense kernel the openai-hub article asks comparisons to use:
+ * O[t] = sum_{j <= t} softmax_j(scale * Q[t] . K[j]) V[j], fp32 output.
+ * Uses batch, heads, T, d and scale of cfg (d = 32, 64, 128 or 256; other
+ * built sizes return ALHR_ERR_UNSUPPORTED); the routing fields are checked
+ * as for the other calls but not used. */
+alhr_status alhr_dense_attend(const alhr_config *cfg, const int8_t *Q,
+                              const int8_t *K, const float *V, float *O,
+                              void *stream);
+
 /* Static text for a status code. */
 const char *alhr_status_string(alhr_status status);
 

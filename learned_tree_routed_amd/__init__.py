@@ -22,8 +22,8 @@ __all__ = [
     "Config", "AlhrError", "lib_path", "load",
     "alhr_workspace_bytes", "alhr_build_tree", "alhr_predict_budget", "alhr_route",
     "alhr_route_stats", "alhr_sparse_attend", "alhr_route_attend", "alhr_forward",
-    "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_status_string",
-    "alhr_last_error", "alhr_version", "EXPORTED",
+    "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_dense_attend",
+    "alhr_status_string", "alhr_last_error", "alhr_version", "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,8 +33,8 @@ _LIB_PATH = os.path.join(_HERE, "libalhr.so")
 EXPORTED = (
     "alhr_workspace_bytes", "alhr_build_tree", "alhr_predict_budget", "alhr_route",
     "alhr_route_stats", "alhr_sparse_attend", "alhr_route_attend", "alhr_forward",
-    "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_status_string",
-    "alhr_last_error", "alhr_version",
+    "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_dense_attend",
+    "alhr_status_string", "alhr_last_error", "alhr_version",
 )
 
 STATUS = {0: "ALHR_OK", -1: "ALHR_ERR_ARG", -2: "ALHR_ERR_OVERFLOW", -3: "ALHR_ERR_DEVICE",
@@ -116,6 +116,7 @@ def load():
         "alhr_prefix_from_tree": ([cfgp, i32, P, P, P, P], C.c_int),
         "alhr_append": ([cfgp, i32, P, P, P, P, P, P, P], C.c_int),
         "alhr_decode_step": ([cfgp, i32, P, P, P, P, P, P, i32, P, P, P, P, P], C.c_int),
+        "alhr_dense_attend": ([cfgp, P, P, P, P, P], C.c_int),
         "alhr_status_string": ([C.c_int], C.c_char_p),
         "alhr_last_error": ([], C.c_char_p),
         "alhr_version": ([], i32),
@@ -356,3 +357,16 @@ def alhr_decode_step(cfg, pos, q_new, K, V, nodes, prefix, W=None, fixed_budget=
           _ptr(nodes), _ptr(prefix), _ptr(W), int(fixed_budget), _ptr(budget), _ptr(idx),
           _ptr(count), _ptr(O), _stream(stream))
     return idx, count, O
+
+
+def alhr_dense_attend(cfg, Q, K, V, O=None, stream=None):
+    """Dense causal softmax attention over every past key (the baseline)."""
+    torch = _torch()
+    rows, _, _ = _shapes(cfg)
+    _check("Q", Q, torch.int8, rows)
+    _check("K", K, torch.int8, rows, Q.device)
+    _check("V", V, torch.float32, rows, Q.device)
+    O = _out(O, "O", torch.float32, rows, Q.device)
+    _call("alhr_dense_attend", C.byref(cfg.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
+          _stream(stream))
+    return O

@@ -30,7 +30,7 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
 ]
 
-SOURCES = ["api.hip", "build.hip", "predict.hip", "route.hip", "decode.hip"]
+SOURCES = ["api.hip", "build.hip", "predict.hip", "route.hip", "decode.hip", "dense.hip"]
 
 
 def _run(cmd):

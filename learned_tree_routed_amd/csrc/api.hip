@@ -282,6 +282,23 @@ alhr_status alhr_forward(const alhr_config* cfg, const int8_t* Q, const int8_t* 
     return device_status(fn, e);
 }
 
+alhr_status alhr_dense_attend(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
+                              const float* V, float* O, void* stream)
+{
+    const char* fn = "alhr_dense_attend";
+    alhr::Shape s;
+    if (alhr_status st = check_config(fn, cfg, &s)) return st;
+    if (cfg->d < 32)
+        return fail(ALHR_ERR_UNSUPPORTED, "%s: d = %d is not built for the dense kernel (32, 64, "
+                                          "128, 256)", fn, cfg->d);
+    ALHR_NEED_PTR(Q);
+    ALHR_NEED_PTR(K);
+    ALHR_NEED_PTR(V);
+    ALHR_NEED_PTR(O);
+    (void)hipGetLastError();
+    return device_status(fn, alhr::launch_dense(s, Q, K, V, O, as_stream(stream)));
+}
+
 alhr_status alhr_prefix_from_tree(const alhr_config* cfg, int32_t n, const int8_t* K,
                                   const int32_t* nodes, int32_t* prefix, void* stream)
 {

@@ -47,4 +47,7 @@ hipError_t launch_decode(const Shape& s, int pos, const int8_t* q_new, const int
                          const int8_t* W, int fixed_budget, int32_t* budget, int32_t* idx,
                          int32_t* count, float* O, hipStream_t st);
 
+hipError_t launch_dense(const Shape& s, const int8_t* Q, const int8_t* K, const float* V, float* O,
+                        hipStream_t st);
+
 }  // namespace alhr

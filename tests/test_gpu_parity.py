@@ -293,3 +293,63 @@ def test_invalid_arguments_rejected_on_device(torch_dev):
     with pytest.raises(alhr.AlhrError) as e:
         alhr.alhr_build_tree(bad, torch.zeros((1, 1, 64, 48), dtype=torch.int8, device=dev))
     assert e.value.status == -4
+
+
+# ------------------------------------------------------- dense baseline ---
+def dense_oracle_rows(Q, K, V, scale, ts):
+    """The oracle's attention over all past keys for the queries ts."""
+    return np.stack([oracle.attend(np.arange(t + 1, dtype=np.int32), Q[t], K, V, scale) for t in ts])
+
+
+@pytest.mark.parametrize("T,d", [(16, 32), (64, 32), (256, 64), (128, 128), (64, 256), (1024, 64)])
+def test_dense_attention_every_query(torch_dev, T, d):
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    w = Workload("dense", 21, 2, 2, T, d, "clustered")
+    Q, K, V, _ = host_inputs(w)
+    cfg = w.config()
+    q, k, v = to_dev(torch, dev, Q, K, V)
+    say("alhr_dense_attend B2 H2 T%d d%d" % (T, d))
+    O = alhr.alhr_dense_attend(cfg, q, k, v)
+    torch.cuda.synchronize()
+    O = O.cpu().numpy()
+    for b in range(2):
+        for h in range(2):
+            ref = dense_oracle_rows(Q[b, h], K[b, h], V[b, h], cfg.scale, range(T))
+            err = np.abs(O[b, h] - ref).max()
+            assert err <= ATOL, "pair (%d, %d): max |O - oracle| = %g" % (b, h, err)
+
+
+def test_dense_attention_full_size_sampled(torch_dev):
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    w = WORKLOADS["t16k"]
+    Q, K, V, _ = host_inputs(w)
+    cfg = w.config()
+    q, k, v = to_dev(torch, dev, Q, K, V)
+    say("alhr_dense_attend t16k")
+    O = alhr.alhr_dense_attend(cfg, q, k, v)
+    torch.cuda.synchronize()
+    O = O.cpu().numpy()
+    rng = np.random.default_rng(3)
+    for h in (0, 3, 7):
+        ts = sorted(set(rng.choice(w.T, 24, replace=False).tolist()) | {0, 31, 32, w.T - 1})
+        ref = dense_oracle_rows(Q[0, h], K[0, h], V[0, h], cfg.scale, ts)
+        err = np.abs(O[0, h, ts] - ref).max()
+        assert err <= ATOL, "head %d: max |O - oracle| = %g" % (h, err)
+
+
+def test_dense_equals_routing_with_full_budget(torch_dev):
+    """With the budget covering every past key the routed path is dense
+    attention: both kernels must agree on the same inputs."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    T = 64
+    w = Workload("dense_vs_route", 22, 1, 4, T, 64, "clustered", fixed_budget=64)
+    Q, K, V, _ = host_inputs(w)
+    cfg = w.config()
+    q, k, v = to_dev(torch, dev, Q, K, V)
+    dense = alhr.alhr_dense_attend(cfg, q, k, v)
+    routed = alhr.alhr_forward(cfg, q, k, v, None, fixed_budget=64)
+    torch.cuda.synchronize()
+    assert (dense - routed["O"]).abs().max().item() <= 1e-5
