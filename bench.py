@@ -73,11 +73,13 @@ def read_traffic(bytes_unit=1024):
 def bytes_per_query(stats, cfg, budget_read=True):
     """Algorithmic bytes of the fused kernel per query from its load counts:
     q row, neighbour key rows, tree rows loaded (left children and cover
-    roots, int32), key rows loaded by the descent, value rows (fp32), the
-    output row, the idx row and the count (and the budget it reads)."""
+    roots; 4d bytes for int32 rows, 2d for int16 rows), key rows loaded by
+    the descent, value rows (fp32), the output row, the idx row and the
+    count (and the budget it reads)."""
     d = cfg.d
-    tree_rows, key_rows, n, C = (stats[..., i].astype(np.int64) for i in range(4))
-    b = (d + n * d + tree_rows * 4 * d + key_rows * d + C * 4 * d + 4 * d
+    rows32, rows16, key_rows, C = (stats[..., i].astype(np.int64) for i in range(4))
+    n = np.minimum(cfg.window, C)
+    b = (d + n * d + rows32 * 4 * d + rows16 * 2 * d + key_rows * d + C * 4 * d + 4 * d
          + 4 * cfg.max_budget + 4 + (4 if budget_read else 0))
     return b
 
@@ -194,8 +196,9 @@ def bench_prefill(args, torch, dev):
             "kernel": "alhr_dense_attend (causal, int8 MFMA scores, fp32 MFMA values)",
             "ms": dense_ms, "routed_step_speedup": dense_ms / ms_step},
         "diagnostics": {"mean_budget": float(bud.mean()), "mean_keys_per_query": float(cnt.mean()),
-                        "mean_tree_rows_loaded": float(stats[..., 0].mean()),
-                        "mean_key_rows_loaded": float(stats[..., 1].mean()),
+                        "mean_tree_rows_loaded_int32": float(stats[..., 0].mean()),
+                        "mean_tree_rows_loaded_int16": float(stats[..., 1].mean()),
+                        "mean_key_rows_loaded": float(stats[..., 2].mean()),
                         "bytes_per_query": bpl / queries,
                         "compression_T_over_keys": float(w.T / cnt.mean()),
                         "compression_causal_over_keys": float((w.T + 1) / 2 / cnt.mean())},
@@ -344,7 +347,7 @@ def bench_sweep(args, torch, dev):
                       "routed_qps": q / (ms * 1e-3),
                       "route_attend_GBps": bpl / (kms * 1e-3) / 1e9,
                       "mean_keys": float(cnt.float().mean().item()),
-                      "mean_tree_rows": float(stats[..., 0].mean()),
+                      "mean_tree_rows": float(stats[..., 0].mean() + stats[..., 1].mean()),
                       "cache_bytes_K_V_tree": state,
                       "dense_ms": dense_ms, "dense_over_routed_step": dense_ms / ms})
         Ts.append(T)

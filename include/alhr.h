@@ -34,7 +34,21 @@
  *          node (level l >= 1, index p), covering keys [p*2^l, (p+1)*2^l),
  *          is row (T >> l) + p; row 1 is the root; row 0 is never written;
  *          the children of row i are rows 2i and 2i+1, and a row number
- *          h >= T stands for key row h - T.
+ *          h >= T stands for key row h - T.  Compact encoding: with
+ *          l16 = alhr_tree_int16_levels(cfg) (the levels whose sums
+ *          provably fit int16: kmax * 2^l <= 32767) and b = T >> l16, a row
+ *          i < b (levels above l16) holds d int32 at byte offset 4*d*i of
+ *          the pair's table, and a row i >= b (levels 1..l16) holds d int16
+ *          at byte offset 4*d*b + 2*d*(i - b), packed densely; the last
+ *          2*d*(T - b) bytes of the table are left untouched.  The buffer
+ *          size is T * d * 4 bytes per pair either way.  Column order: an
+ *          int16 row is in natural order; an int32 row's d/4 16-byte slots
+ *          (slot g = columns 4g .. 4g+3) are block-interleaved: with
+ *          m = d/16, slot g is stored at slot
+ *          (2 * ((g/2) / m) + g%2) * m + (g/2) % m  (identity at d = 16),
+ *          which lets the scoring kernels read every row with contiguous
+ *          loads.  Callers treat `nodes` as opaque and fill it with
+ *          alhr_build_tree / alhr_append.
  *   budget int32 [batch, heads, T]        keys asked for by each query
  *   idx    int32 [batch, heads, T, max_budget]   selected key positions,
  *          ascending, padded with -1
@@ -93,6 +107,10 @@ typedef struct alhr_config {
 
 /* Bytes of scratch that alhr_predict_budget / alhr_forward need (a multiple
  * of 256; 0 if cfg is invalid). */
+
+/* Number of tree levels stored as int16 rows (see `nodes` above), or -1 if
+ * cfg is invalid. */
+int32_t alhr_tree_int16_levels(const alhr_config *cfg);
 size_t alhr_workspace_bytes(const alhr_config *cfg);
 
 /* Tree of key sums (README, opening paragraph and "Inference stage": one
@@ -125,9 +143,10 @@ alhr_status alhr_route(const alhr_config *cfg, const int8_t *Q,
                        int32_t *idx, int32_t *count, void *stream);
 
 /* Per-query load counts of the routing step, for byte accounting: stats is
- * int32 [batch, heads, T, 4] = (tree rows loaded, key rows loaded in the
- * descent, neighbour key rows, selected keys).  Same arguments as
- * alhr_route; idx and count are written as by alhr_route. */
+ * int32 [batch, heads, T, 4] = (int32 tree rows loaded, int16 tree rows
+ * loaded, key rows loaded by the descent, selected keys C); the neighbour
+ * key rows are min(window, C).  Same arguments as alhr_route; idx and count
+ * are written as by alhr_route. */
 alhr_status alhr_route_stats(const alhr_config *cfg, const int8_t *Q,
                              const int8_t *K, const int32_t *nodes,
                              const int32_t *budget, int32_t fixed_budget,

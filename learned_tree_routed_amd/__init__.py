@@ -23,7 +23,8 @@ __all__ = [
     "alhr_workspace_bytes", "alhr_build_tree", "alhr_predict_budget", "alhr_route",
     "alhr_route_stats", "alhr_sparse_attend", "alhr_route_attend", "alhr_forward",
     "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_dense_attend",
-    "alhr_status_string", "alhr_last_error", "alhr_version", "EXPORTED",
+    "alhr_status_string", "alhr_last_error", "alhr_version", "alhr_tree_int16_levels",
+    "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +35,7 @@ EXPORTED = (
     "alhr_workspace_bytes", "alhr_build_tree", "alhr_predict_budget", "alhr_route",
     "alhr_route_stats", "alhr_sparse_attend", "alhr_route_attend", "alhr_forward",
     "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_dense_attend",
-    "alhr_status_string", "alhr_last_error", "alhr_version",
+    "alhr_status_string", "alhr_last_error", "alhr_version", "alhr_tree_int16_levels",
 )
 
 STATUS = {0: "ALHR_OK", -1: "ALHR_ERR_ARG", -2: "ALHR_ERR_OVERFLOW", -3: "ALHR_ERR_DEVICE",
@@ -120,6 +121,7 @@ def load():
         "alhr_status_string": ([C.c_int], C.c_char_p),
         "alhr_last_error": ([], C.c_char_p),
         "alhr_version": ([], i32),
+        "alhr_tree_int16_levels": ([cfgp], i32),
     }
     for name, (args, res) in sigs.items():
         f = getattr(lib, name)
@@ -184,6 +186,12 @@ def _shapes(cfg):
 # ------------------------------------------------------------ entry points --
 def alhr_workspace_bytes(cfg: Config) -> int:
     return int(load().alhr_workspace_bytes(C.byref(cfg.c())))
+
+
+def alhr_tree_int16_levels(cfg: Config) -> int:
+    """Tree levels 1..l16 are stored as int16 rows (the nodes layout in
+    include/alhr.h); -1 for an invalid configuration."""
+    return int(load().alhr_tree_int16_levels(C.byref(cfg.c())))
 
 
 def alhr_status_string(status: int) -> str:

@@ -39,6 +39,14 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
             return fail(ALHR_ERR_ARG, "%s: argument '%s' is not 16-byte aligned", fn, #p); \
     } while (0)
 
+// Levels whose node sums fit int16: largest l <= L with kmax * 2^l <= 32767.
+int int16_levels(int kmax, int L)
+{
+    int l = 0;
+    while (l < L && (int64_t)kmax * ((int64_t)2 << l) <= 32767) ++l;
+    return l;
+}
+
 alhr_status check_config(const char* fn, const alhr_config* c, alhr::Shape* s)
 {
     if (!c) return fail(ALHR_ERR_ARG, "%s: cfg is NULL", fn);
@@ -92,6 +100,7 @@ alhr_status check_config(const char* fn, const alhr_config* c, alhr::Shape* s)
         s->scale = c->scale;
         // every scored node has at most T/2 keys: its entries fit 24 signed bits?
         s->mul24 = (int64_t)c->kmax * (T / 2) < ((int64_t)1 << 23);
+        s->l16 = int16_levels(c->kmax, L);
     }
     return ALHR_OK;
 }
@@ -135,6 +144,13 @@ const char* alhr_status_string(alhr_status s)
 }
 
 const char* alhr_last_error(void) { return g_last_error.c_str(); }
+
+int32_t alhr_tree_int16_levels(const alhr_config* cfg)
+{
+    alhr::Shape s;
+    if (check_config("alhr_tree_int16_levels", cfg, &s) != ALHR_OK) return -1;
+    return s.l16;
+}
 
 size_t alhr_workspace_bytes(const alhr_config* cfg)
 {

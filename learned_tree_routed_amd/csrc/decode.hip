@@ -16,6 +16,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxLevels = 20;   // T <= 2^20
 
+__device__ __forceinline__ int pack16(int lo, int hi) { return (lo & 0xFFFF) | (hi << 16); }
+__device__ __forceinline__ int lo16(int w) { return (int)(short)(w & 0xFFFF); }
+__device__ __forceinline__ int hi16(int w) { return w >> 16; }
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_append(const int8_t* __restrict__ k_new,
                                                      const float* __restrict__ v_new,
@@ -23,7 +27,7 @@ __global__ __launch_bounds__(kThreads) void k_append(const int8_t* __restrict__ 
                                                      float* __restrict__ V,
                                                      int32_t* __restrict__ nodes,
                                                      int32_t* __restrict__ prefix, int P, int T,
-                                                     int L, int pos)
+                                                     int L, int l16, int pos)
 {
     constexpr int C4 = D / 4;
     const int gid = blockIdx.x * kThreads + threadIdx.x;
@@ -31,35 +35,54 @@ __global__ __launch_bounds__(kThreads) void k_append(const int8_t* __restrict__ 
     const int pair = gid / C4, g = gid % C4;
     const int kw = reinterpret_cast<const int*>(k_new)[(size_t)pair * C4 + g];
     const int4 kv = make_int4(sbyte(kw, 0), sbyte(kw, 1), sbyte(kw, 2), sbyte(kw, 3));
+    // key bytes of the even and the odd thread of this thread's pair g, g ^ 1
+    // (C4 is even, so both belong to the same (batch, head) pair)
+    const int kw_partner = __shfl_xor(kw, 1);
+    const int kw_even = (g & 1) ? kw_partner : kw, kw_odd = (g & 1) ? kw : kw_partner;
     const size_t row = (size_t)pair * T + pos;
     reinterpret_cast<int*>(K)[row * C4 + g] = kw;
     reinterpret_cast<float4*>(V)[row * C4 + g] =
         reinterpret_cast<const float4*>(v_new)[(size_t)pair * C4 + g];
-    // all L ancestor cells are loaded before any is stored, so the loads are
-    // in flight together instead of one dependent round trip per level
-    int4* tree = reinterpret_cast<int4*>(nodes) + (size_t)pair * T * C4;
+    // All L ancestor cells (and the running sum) are loaded before anything
+    // is stored, so the loads are in flight together instead of one
+    // dependent round trip per level.  Levels 1..l16 hold int16 rows, higher
+    // levels int32.  No load or store sits in a branch (a branch around a
+    // memory access makes the next one wait for it): every level is one
+    // 16-byte load and one 16-byte store at a selected address.  At an int16
+    // level, threads g and g ^ 1 share one 16-byte chunk (8 columns) and
+    // both write the same updated chunk.  The level loop runs to kMaxLevels
+    // with the level clamped to L, so it has no branch either: the extra
+    // iterations re-read and re-write the root with the same value.
+    int32_t* tree = nodes + (size_t)pair * T * D;
+    int4* pre = reinterpret_cast<int4*>(prefix) + (size_t)pair * C4 + g;
+    int4* cell_at[kMaxLevels];
     int4 cells[kMaxLevels];
 #pragma unroll
-    for (int l = 1; l <= kMaxLevels; ++l)
-        if (l <= L) cells[l - 1] = tree[(size_t)((T >> l) + (pos >> l)) * C4 + g];
-#pragma unroll
-    for (int l = 1; l <= kMaxLevels; ++l) {
-        if (l <= L) {
-            int4 v = cells[l - 1];
-            v.x += kv.x;
-            v.y += kv.y;
-            v.z += kv.z;
-            v.w += kv.w;
-            tree[(size_t)((T >> l) + (pos >> l)) * C4 + g] = v;
-        }
+    for (int i = 1; i <= kMaxLevels; ++i) {
+        const int l = i < L ? i : L;
+        const size_t r = (size_t)((T >> l) + (pos >> l));
+        cell_at[i - 1] = l <= l16
+            ? reinterpret_cast<int4*>(const_cast<int32_t*>(tree_row16<D>(tree, T, l16, r))) +
+                  (g >> 1)
+            : reinterpret_cast<int4*>(tree + r * D) + wide_slot<D>(g);
+        cells[i - 1] = *cell_at[i - 1];
     }
-    int4* pre = reinterpret_cast<int4*>(prefix) + (size_t)pair * C4 + g;
-    int4 p = *pre;
-    p.x += kv.x;
-    p.y += kv.y;
-    p.z += kv.z;
-    p.w += kv.w;
-    *pre = p;
+    const int4 p = *pre;
+#pragma unroll
+    for (int i = 1; i <= kMaxLevels; ++i) {
+        const int l = i < L ? i : L;
+        const int4 c = cells[i - 1];
+        const int4 wide = make_int4(c.x + kv.x, c.y + kv.y, c.z + kv.z, c.w + kv.w);
+        const int4 narrow = make_int4(
+            pack16(lo16(c.x) + sbyte(kw_even, 0), hi16(c.x) + sbyte(kw_even, 1)),
+            pack16(lo16(c.y) + sbyte(kw_even, 2), hi16(c.y) + sbyte(kw_even, 3)),
+            pack16(lo16(c.z) + sbyte(kw_odd, 0), hi16(c.z) + sbyte(kw_odd, 1)),
+            pack16(lo16(c.w) + sbyte(kw_odd, 2), hi16(c.w) + sbyte(kw_odd, 3)));
+        const bool nar = l <= l16;   // per-component select, no int4 temporary
+        *cell_at[i - 1] = make_int4(nar ? narrow.x : wide.x, nar ? narrow.y : wide.y,
+                                    nar ? narrow.z : wide.z, nar ? narrow.w : wide.w);
+    }
+    *pre = make_int4(p.x + kv.x, p.y + kv.y, p.z + kv.z, p.w + kv.w);
 }
 
 // prefix[pair] = sum of the maximal complete subtrees covering [0, n).
@@ -67,7 +90,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void k_prefix_from_tree(const int8_t* __restrict__ K,
                                                                const int32_t* __restrict__ nodes,
                                                                int32_t* __restrict__ prefix,
-                                                               int P, int T, int L, int n)
+                                                               int P, int T, int L, int l16,
+                                                               int n)
 {
     constexpr int C4 = D / 4;
     const int gid = blockIdx.x * kThreads + threadIdx.x;
@@ -85,8 +109,16 @@ __global__ __launch_bounds__(kThreads) void k_prefix_from_tree(const int8_t* __r
             acc.z += sbyte(kw, 2);
             acc.w += sbyte(kw, 3);
         } else {
-            const int4 v = reinterpret_cast<const int4*>(
-                nodes)[((size_t)pair * T + (T >> l) + (start >> l)) * C4 + g];
+            const int32_t* tree = nodes + (size_t)pair * T * D;
+            const size_t r = (size_t)((T >> l) + (start >> l));
+            const int32_t* row = l <= l16 ? tree_row16<D>(tree, T, l16, r) : tree_row32<D>(tree, r);
+            int4 v;
+            if (l <= l16) {
+                const int2 w = reinterpret_cast<const int2*>(row)[g];
+                v = make_int4(lo16(w.x), hi16(w.x), lo16(w.y), hi16(w.y));
+            } else {
+                v = reinterpret_cast<const int4*>(row)[wide_slot<D>(g)];
+            }
             acc.x += v.x;
             acc.y += v.y;
             acc.z += v.z;
@@ -106,7 +138,7 @@ hipError_t launch_append(const Shape& s, int pos, const int8_t* k_new, const flo
     const dim3 grid(blocks_for(s.P, s.d));
 #define ALHR_APPEND(DD)                                                                        \
     hipLaunchKernelGGL((k_append<DD>), grid, dim3(kThreads), 0, st, k_new, v_new, K, V, nodes, \
-                       prefix, s.P, s.T, s.L, pos)
+                       prefix, s.P, s.T, s.L, s.l16, pos)
     switch (s.d) {
         case 16: ALHR_APPEND(16); break;
         case 32: ALHR_APPEND(32); break;
@@ -125,7 +157,7 @@ hipError_t launch_prefix_from_tree(const Shape& s, int n, const int8_t* K, const
     const dim3 grid(blocks_for(s.P, s.d));
 #define ALHR_PREFIX(DD)                                                                       \
     hipLaunchKernelGGL((k_prefix_from_tree<DD>), grid, dim3(kThreads), 0, st, K, nodes, prefix, \
-                       s.P, s.T, s.L, n)
+                       s.P, s.T, s.L, s.l16, n)
     switch (s.d) {
         case 16: ALHR_PREFIX(16); break;
         case 32: ALHR_PREFIX(32); break;

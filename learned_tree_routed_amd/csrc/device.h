@@ -123,6 +123,40 @@ template <typename T> __device__ __forceinline__ T wave_max(T v)
     return v;
 }
 
+// ---- tree table layout ----------------------------------------------------
+// One pair's table is T * d * 4 bytes.  Heap row r (node (l, p) is row
+// (T >> l) + p) of a level l > l16 is d int32 at byte r * 4d; rows of levels
+// 1..l16 (r >= T >> l16) are d int16, packed densely after the int32 rows:
+// byte (T >> l16) * 4d + (r - (T >> l16)) * 2d.
+//
+// Column order inside an int32 row: its d/4 16-byte slots form 4 blocks of
+// LPR = d/16 slots, and the natural slot g = 2c + h (8-column chunk c, half
+// h) is stored at slot (2 * (c / LPR) + h) * LPR + c % LPR.  Lane s of a row
+// group (which holds the query for chunks s and LPR + s) then reads slots
+// s, LPR + s, 2 LPR + s and 3 LPR + s, so each of its four loads covers one
+// contiguous block of the row.  int16 rows keep the natural order: chunk c
+// is slot c.
+template <int D>
+__host__ __device__ constexpr int wide_slot(int g)
+{
+    constexpr int LPR = D / 16;
+    return (2 * ((g >> 1) / LPR) + (g & 1)) * LPR + (g >> 1) % LPR;
+}
+
+template <int D>
+__device__ __forceinline__ const int32_t* tree_row32(const int32_t* pair_table, size_t r)
+{
+    return pair_table + r * D;
+}
+template <int D>
+__device__ __forceinline__ const int32_t* tree_row16(const int32_t* pair_table, int T, int l16,
+                                                     size_t r)
+{
+    const size_t b16 = (size_t)(T >> l16);
+    return reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(pair_table) +
+                                            b16 * 4 * D + (r - b16) * 2 * D);
+}
+
 __device__ __forceinline__ int dot4_i8(int a, int b, int acc)
 {
     return __builtin_amdgcn_sdot4(a, b, acc, false);

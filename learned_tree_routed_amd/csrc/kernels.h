@@ -18,6 +18,7 @@ struct Shape {
     int max_budget;
     float scale;
     bool mul24;       // every scored tree node fits a signed 24-bit multiply
+    int l16;          // tree levels 1..l16 are stored as int16 rows (kmax * 2^l <= 32767)
 };
 
 // Scratch for the predictor: one int32 per (pair, chunk, class).

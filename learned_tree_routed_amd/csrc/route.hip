@@ -57,9 +57,12 @@ __device__ __forceinline__ int key_start(uint64_t k) { return 0xFFFFF - (int)((u
 __device__ __forceinline__ int key_level(uint64_t k) { return (int)((uint32_t)k & 31u); }
 
 // ---- the query in registers, in the two column layouts used for scoring ---
+// Lane s of a row group (LPR = d / 16 lanes per row) holds the columns of the
+// two 8-column chunks c = k * LPR + s (k < 2) as packed int16 pairs, and the
+// 16 columns 16s .. 16s + 15 as packed int8 (for key rows).
 template <int D>
 struct QueryRegs {
-    int qi[16];   // tree-row columns 4*(k*LPR + s) + e  (k, e < 4)
+    int qh[8];    // columns 8c + 2j, 8c + 2j + 1 of chunk c = k*LPR + s in qh[4k + j]
     int qp[4];    // key-row columns 16*s .. 16*s + 15, packed int8
 };
 
@@ -74,11 +77,23 @@ __device__ __forceinline__ void load_query(const int8_t* __restrict__ q, int s, 
     r.qp[2] = p.z;
     r.qp[3] = p.w;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int w = qw[k * LPR + s];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r.qi[4 * k + e] = sbyte(w, e);
+    for (int k = 0; k < 2; ++k) {
+        const int c = k * LPR + s;
+        const int w0 = qw[2 * c], w1 = qw[2 * c + 1];
+        r.qh[4 * k + 0] = (sbyte(w0, 0) & 0xFFFF) | (sbyte(w0, 1) << 16);
+        r.qh[4 * k + 1] = (sbyte(w0, 2) & 0xFFFF) | (sbyte(w0, 3) << 16);
+        r.qh[4 * k + 2] = (sbyte(w1, 0) & 0xFFFF) | (sbyte(w1, 1) << 16);
+        r.qh[4 * k + 3] = (sbyte(w1, 2) & 0xFFFF) | (sbyte(w1, 3) << 16);
     }
+}
+
+__device__ __forceinline__ int lo16(int w) { return (int)(short)(w & 0xFFFF); }
+__device__ __forceinline__ int hi16(int w) { return w >> 16; }
+
+typedef short v2s __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ int dot2_i16(int a, int b, int acc)
+{
+    return __builtin_amdgcn_sdot2(__builtin_bit_cast(v2s, a), __builtin_bit_cast(v2s, b), acc, false);
 }
 
 template <bool MUL24>
@@ -89,27 +104,56 @@ __device__ __forceinline__ int imul(int a, int b)
 }
 
 // q . node for node (level, start) of one pair; every lane of the row's
-// group receives the full score.  Inactive lanes contribute 0.
+// group receives the full score.  Inactive lanes contribute 0.  Tree rows of
+// levels 1..l16 are int16 (packed after the int32 rows, see tree_row16),
+// higher levels int32, level 0 is the key row.
 template <int D, bool MUL24>
 __device__ __forceinline__ int score_node(const int32_t* __restrict__ nodes_pair,
-                                          const int8_t* __restrict__ keys_pair, int T, int level,
-                                          int start, bool active, int s, const QueryRegs<D>& q)
+                                          const int8_t* __restrict__ keys_pair, int T, int l16,
+                                          int level, int start, bool active, int s,
+                                          const QueryRegs<D>& q)
 {
     constexpr int LPR = D / 16;
     int acc = 0;
     if (active) {
-        if (level > 0) {
+        if (level > l16) {
+            // int32 row (block-interleaved, see wide_slot): block j = 2k + h
+            // holds at slot s the columns 8c + 4h .. 8c + 4h + 3 of chunk
+            // c = k * LPR + s, i.e. the query pairs qh[2j], qh[2j + 1].  The
+            // pairs are unpacked here (these are the few top levels).
             const int4* row = reinterpret_cast<const int4*>(
-                nodes_pair + (size_t)((T >> level) + (start >> level)) * D);
+                tree_row32<D>(nodes_pair, (size_t)((T >> level) + (start >> level))));
             int4 v[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) v[k] = row[k * LPR + s];
+            for (int j = 0; j < 4; ++j) v[j] = row[j * LPR + s];
+            // an opaque copy keeps the unpacking here instead of letting it
+            // be hoisted out of the descent loop into 16 live registers
+            int qh[8];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                acc += imul<MUL24>(q.qi[4 * k + 0], v[k].x);
-                acc += imul<MUL24>(q.qi[4 * k + 1], v[k].y);
-                acc += imul<MUL24>(q.qi[4 * k + 2], v[k].z);
-                acc += imul<MUL24>(q.qi[4 * k + 3], v[k].w);
+            for (int j = 0; j < 8; ++j) {
+                qh[j] = q.qh[j];
+                asm volatile("" : "+v"(qh[j]));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc += imul<MUL24>(lo16(qh[2 * j]), v[j].x);
+                acc += imul<MUL24>(hi16(qh[2 * j]), v[j].y);
+                acc += imul<MUL24>(lo16(qh[2 * j + 1]), v[j].z);
+                acc += imul<MUL24>(hi16(qh[2 * j + 1]), v[j].w);
+            }
+        } else if (level > 0) {
+            // int16 row: chunk c is int4 c
+            const int4* row = reinterpret_cast<const int4*>(
+                tree_row16<D>(nodes_pair, T, l16, (size_t)((T >> level) + (start >> level))));
+            int4 v[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) v[k] = row[k * LPR + s];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                acc = dot2_i16(q.qh[4 * k + 0], v[k].x, acc);
+                acc = dot2_i16(q.qh[4 * k + 1], v[k].y, acc);
+                acc = dot2_i16(q.qh[4 * k + 2], v[k].z, acc);
+                acc = dot2_i16(q.qh[4 * k + 3], v[k].w, acc);
             }
         } else {
             const int4 v = reinterpret_cast<const int4*>(keys_pair + (size_t)start * D)[s];
@@ -232,16 +276,18 @@ __device__ __forceinline__ int select_best(const uint64_t* cand, int n, int r, u
 }
 
 struct RouteCounts {
-    int tree_rows;   // int32 tree rows loaded
-    int key_rows;    // key rows loaded by the descent
+    int tree_rows;     // int32 tree rows loaded
+    int tree16_rows;   // int16 tree rows loaded
+    int key_rows;      // key rows loaded by the descent
 };
 
 // Route query t of one pair.  On return sm.pos[0, C) holds the selected
 // positions in ascending order and sm.score[0, C) their q . K scores.
 template <int D, bool MUL24, bool STATS>
 __device__ int route_query(const int32_t* __restrict__ nodes_pair,
-                           const int8_t* __restrict__ keys_pair, int T, int L, int t, int B,
-                           int window, const QueryRegs<D>& q, WaveLds& sm, RouteCounts& cnt)
+                           const int8_t* __restrict__ keys_pair, int T, int L, int l16, int t,
+                           int B, int window, const QueryRegs<D>& q, WaveLds& sm,
+                           RouteCounts& cnt)
 {
     constexpr int LPR = D / 16, RPG = kWave / LPR;
     const int lane = lane_id();
@@ -255,7 +301,7 @@ __device__ int route_query(const int32_t* __restrict__ nodes_pair,
     for (int base = 0; base < n; base += RPG) {
         const int k = base + g;
         const bool act = k < n;
-        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, 0, m + k, act, s, q);
+        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, l16, 0, m + k, act, s, q);
         if (act && s == 0) {
             sm.pos[r + k] = m + k;
             sm.score[r + k] = sc;
@@ -274,9 +320,10 @@ __device__ int route_query(const int32_t* __restrict__ nodes_pair,
         const int b = base + g;
         const bool act = b < L && ((m >> b) & 1);
         const int start = act ? (m & ~((2 << b) - 1)) : 0;
-        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, b, start, act, s, q);
+        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, l16, b, start, act, s, q);
         if (STATS) {
-            cnt.tree_rows += wave_count(act && s == 0 && b > 0);
+            cnt.tree_rows += wave_count(act && s == 0 && b > l16);
+            cnt.tree16_rows += wave_count(act && s == 0 && b > 0 && b <= l16);
             cnt.key_rows += wave_count(act && s == 0 && b == 0);
         }
         if (b < L && s == 0) sm.cand[L - 1 - b] = act ? make_key(sc, start, b) : 0ull;
@@ -293,9 +340,10 @@ __device__ int route_query(const int32_t* __restrict__ nodes_pair,
             const int lv = key_level(key), st = key_start(key);
             const bool expand = i < nb && lv > 0;
             const int cl = lv - 1;
-            const int left = score_node<D, MUL24>(nodes_pair, keys_pair, T, cl, st, expand, s, q);
+            const int left = score_node<D, MUL24>(nodes_pair, keys_pair, T, l16, cl, st, expand, s, q);
             if (STATS) {
-                cnt.tree_rows += wave_count(expand && s == 0 && cl > 0);
+                cnt.tree_rows += wave_count(expand && s == 0 && cl > l16);
+                cnt.tree16_rows += wave_count(expand && s == 0 && cl > 0 && cl <= l16);
                 cnt.key_rows += wave_count(expand && s == 0 && cl == 0);
             }
             if (i < nb && s == 0) {
@@ -384,7 +432,8 @@ __global__ __launch_bounds__(kThreads) void k_route(
     const int8_t* __restrict__ Q, const int8_t* __restrict__ K, const float* __restrict__ V,
     const int32_t* __restrict__ nodes, const int32_t* __restrict__ budget, int fixed_budget,
     int32_t* __restrict__ idx, int32_t* __restrict__ count, float* __restrict__ O,
-    int32_t* __restrict__ stats, int P, int T, int L, int window, int max_budget, float scale)
+    int32_t* __restrict__ stats, int P, int T, int L, int l16, int window, int max_budget,
+    float scale)
 {
     __shared__ WaveLds smem[kWavesPerBlock];
     const int wid = uniform((int)(threadIdx.x / kWave));
@@ -400,16 +449,15 @@ __global__ __launch_bounds__(kThreads) void k_route(
     int B = uniform(budget ? budget[qrow] : fixed_budget);
     B = B < 1 ? 1 : (B > max_budget ? max_budget : B);
     WaveLds& sm = smem[wid];
-    RouteCounts cnt{0, 0};
+    RouteCounts cnt{0, 0, 0};
     const int C = route_query<D, MUL24, STATS>(nodes + (size_t)pair * T * D,
-                                                K + (size_t)pair * T * D, T, L, t, B, window, q,
-                                                sm, cnt);
+                                                K + (size_t)pair * T * D, T, L, l16, t, B,
+                                                window, q, sm, cnt);
     write_selection(sm, C, max_budget, idx + qrow * max_budget, count + qrow);
     if (STATS && lane_id() == 0) {
-        const int n = window < C ? window : C;
         stats[qrow * 4 + 0] = cnt.tree_rows;
-        stats[qrow * 4 + 1] = cnt.key_rows;
-        stats[qrow * 4 + 2] = n;
+        stats[qrow * 4 + 1] = cnt.tree16_rows;
+        stats[qrow * 4 + 2] = cnt.key_rows;
         stats[qrow * 4 + 3] = C;
     }
     if constexpr (ATTEND)
@@ -447,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(const int8_t* __restrict__ 
         const int c = base + g;
         const int j = c < C ? idx[qrow * max_budget + c] : -1;
         const bool act = c < C && (unsigned)j < (unsigned)T;
-        const int sc = score_node<D, false>(nullptr, keys_pair, T, 0, act ? j : 0, act, s, q);
+        const int sc = score_node<D, false>(nullptr, keys_pair, T, 0, 0, act ? j : 0, act, s, q);
         if (c < C && s == 0) {
             sm.pos[c] = j;
             sm.score[c] = sc;
@@ -502,8 +550,9 @@ struct BlockShared {
 
 template <int D, bool MUL24>
 __device__ int route_query_block(const int32_t* __restrict__ nodes_pair,
-                                 const int8_t* __restrict__ keys_pair, int T, int L, int t, int B,
-                                 int window, const QueryRegs<D>& q, BlockShared& bs)
+                                 const int8_t* __restrict__ keys_pair, int T, int L, int l16,
+                                 int t, int B, int window, const QueryRegs<D>& q,
+                                 BlockShared& bs)
 {
     constexpr int LPR = D / 16, RPG = kWave / LPR, RPB = RPG * kDecodeWaves;
     WaveLds& sm = bs.sm;
@@ -513,13 +562,11 @@ __device__ int route_query_block(const int32_t* __restrict__ nodes_pair,
     const int n = uniform(window < C ? window : C);
     const int r = C - n;
     const int m = t + 1 - n;
-    RouteCounts unused{0, 0};
-    (void)unused;
 
     for (int base = 0; base < n; base += RPB) {
         const int k = base + e0;
         const bool act = k < n;
-        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, 0, m + k, act, s, q);
+        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, l16, 0, m + k, act, s, q);
         if (act && s == 0) {
             sm.pos[r + k] = m + k;
             sm.score[r + k] = sc;
@@ -533,7 +580,7 @@ __device__ int route_query_block(const int32_t* __restrict__ nodes_pair,
         const int b = base + e0;
         const bool act = b < L && ((m >> b) & 1);
         const int start = act ? (m & ~((2 << b) - 1)) : 0;
-        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, b, start, act, s, q);
+        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, l16, b, start, act, s, q);
         if (b < L && s == 0) sm.cand[L - 1 - b] = act ? make_key(sc, start, b) : 0ull;
     }
     __syncthreads();
@@ -557,7 +604,7 @@ __device__ int route_query_block(const int32_t* __restrict__ nodes_pair,
             const int lv = key_level(key), st = key_start(key);
             const bool expand = i < nb && lv > 0;
             const int cl = lv - 1;
-            const int left = score_node<D, MUL24>(nodes_pair, keys_pair, T, cl, st, expand, s, q);
+            const int left = score_node<D, MUL24>(nodes_pair, keys_pair, T, l16, cl, st, expand, s, q);
             if (i < nb && s == 0) {
                 if (expand) {
                     sm.cand[2 * i] = make_key(left, st, cl);
@@ -641,12 +688,12 @@ __device__ void attend_block(BlockShared& bs, int C, int T, float scale,
 }
 
 template <int D, bool MUL24>
-__global__ __launch_bounds__(kDecodeWaves * kWave) void k_decode(
+__global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_num_sgpr(80))) void k_decode(
     const int8_t* __restrict__ q_new, const int8_t* __restrict__ K, const float* __restrict__ V,
     const int32_t* __restrict__ nodes, const int32_t* __restrict__ prefix,
     const int8_t* __restrict__ W, int fixed_budget, int32_t* __restrict__ budget_out,
     int32_t* __restrict__ idx, int32_t* __restrict__ count, float* __restrict__ O, int P, int T,
-    int L, int pos, int window, int nc, int kpc, int max_budget, float scale)
+    int L, int l16, int pos, int window, int nc, int kpc, int max_budget, float scale)
 {
     __shared__ BlockShared bs;
     const uint32_t pair = xcd_logical_block();
@@ -667,8 +714,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void k_decode(
     __syncthreads();
     const int B = uniform(bs.budget);
     const int C = route_query_block<D, MUL24>(nodes + (size_t)pair * T * D,
-                                               K + (size_t)pair * T * D, T, L, pos, B, window, q,
-                                               bs);
+                                               K + (size_t)pair * T * D, T, L, l16, pos, B,
+                                               window, q, bs);
     if (wv == 0) write_selection(bs.sm, C, max_budget, idx + (size_t)pair * max_budget, count + pair);
     attend_block<D>(bs, C, T, scale, V + (size_t)pair * T * D, O + (size_t)pair * D);
 }
@@ -689,15 +736,15 @@ hipError_t route_d(const Shape& s, const int8_t* Q, const int8_t* K, const float
     if (stats)
         hipLaunchKernelGGL((k_route<D, MUL24, false, true>), grid, dim3(kThreads), 0, st, Q, K, V,
                            nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T, s.L,
-                           s.window, s.max_budget, s.scale);
+                           s.l16, s.window, s.max_budget, s.scale);
     else if (O)
         hipLaunchKernelGGL((k_route<D, MUL24, true, false>), grid, dim3(kThreads), 0, st, Q, K, V,
                            nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T, s.L,
-                           s.window, s.max_budget, s.scale);
+                           s.l16, s.window, s.max_budget, s.scale);
     else
         hipLaunchKernelGGL((k_route<D, MUL24, false, false>), grid, dim3(kThreads), 0, st, Q, K,
                            V, nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T, s.L,
-                           s.window, s.max_budget, s.scale);
+                           s.l16, s.window, s.max_budget, s.scale);
     return hipGetLastError();
 }
 
@@ -721,12 +768,12 @@ hipError_t decode_d(const Shape& s, int pos, const int8_t* q_new, const int8_t* 
     const dim3 grid((unsigned)((s.P + kXcds - 1) / kXcds * kXcds));
     if (s.mul24)
         hipLaunchKernelGGL((k_decode<D, true>), grid, dim3(kDecodeWaves * kWave), 0, st, q_new, K, V, nodes,
-                           prefix, W, fixed_budget, budget, idx, count, O, s.P, s.T, s.L, pos,
-                           s.window, s.n_classes, s.keys_per_class, s.max_budget, s.scale);
+                           prefix, W, fixed_budget, budget, idx, count, O, s.P, s.T, s.L, s.l16,
+                           pos, s.window, s.n_classes, s.keys_per_class, s.max_budget, s.scale);
     else
         hipLaunchKernelGGL((k_decode<D, false>), grid, dim3(kDecodeWaves * kWave), 0, st, q_new, K, V, nodes,
-                           prefix, W, fixed_budget, budget, idx, count, O, s.P, s.T, s.L, pos,
-                           s.window, s.n_classes, s.keys_per_class, s.max_budget, s.scale);
+                           prefix, W, fixed_budget, budget, idx, count, O, s.P, s.T, s.L, s.l16,
+                           pos, s.window, s.n_classes, s.keys_per_class, s.max_budget, s.scale);
     return hipGetLastError();
 }
 

@@ -39,10 +39,16 @@ class RouteStats(C.Structure):
         ("rounds", C.c_int64),
         ("neighbours", C.c_int64),
         ("count", C.c_int64),
+        ("cover_by_level", C.c_int64 * 24),
+        ("child_by_level", C.c_int64 * 24),
     ]
 
     def as_dict(self):
-        return {f: int(getattr(self, f)) for f, _ in self._fields_}
+        out = {}
+        for f, _ in self._fields_:
+            v = getattr(self, f)
+            out[f] = [int(x) for x in v] if f.endswith("_by_level") else int(v)
+        return out
 
 
 def build(force: bool = True) -> str:

@@ -60,6 +60,8 @@ typedef struct {
     int64_t rounds;           /* beam expansion rounds                         */
     int64_t neighbours;       /* n_t                                          */
     int64_t count;            /* C_t                                          */
+    int64_t cover_by_level[24];   /* cover roots per level                    */
+    int64_t child_by_level[24];   /* expanded children per level              */
 } alhr_ref_route_stats;
 
 static int is_pow2(int64_t x) { return x >= 2 && (x & (x - 1)) == 0; }
@@ -231,7 +233,10 @@ int32_t alhr_ref_route(int32_t T, int32_t d, int32_t window, int32_t t,
                 beam[nb].level = l;
                 beam[nb].start = a;
                 beam[nb].score = score_node(T, d, q, K, nodes, l, a);
-                if (st) { if (l > 0) st->cover_internal++; else st->cover_leaf++; }
+                if (st) {
+                    if (l > 0) st->cover_internal++; else st->cover_leaf++;
+                    st->cover_by_level[l]++;
+                }
                 ++nb;
                 a += (int64_t)1 << l;
             }
@@ -255,7 +260,10 @@ int32_t alhr_ref_route(int32_t T, int32_t d, int32_t window, int32_t t,
                     cand[nc].level = cl;
                     cand[nc].start = cs;
                     cand[nc].score = score_node(T, d, q, K, nodes, cl, cs);
-                    if (st) { if (cl > 0) st->child_internal++; else st->child_leaf++; }
+                    if (st) {
+                        if (cl > 0) st->child_internal++; else st->child_leaf++;
+                        st->child_by_level[cl]++;
+                    }
                     ++nc;
                 }
             }

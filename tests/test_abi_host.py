@@ -31,7 +31,7 @@ def _gpu_visible():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(alhr_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(alhr_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declarations_match_binding():
@@ -189,3 +189,17 @@ def test_python_binding_requires_device_tensors():
         alhr.alhr_build_tree(c, K)
     with pytest.raises(TypeError):
         alhr.alhr_build_tree(c, K.float())
+
+
+def test_int16_tree_levels_follow_the_key_bound():
+    """Levels whose sums fit int16 (kmax * 2^l <= 32767) are stored compactly."""
+    c = alhr.Config(batch=1, heads=1, T=1 << 14, d=64, kmax=8)
+    assert alhr.alhr_tree_int16_levels(c) == 11          # 8 * 2^11 = 16384, 8 * 2^12 = 32768
+    c.T = 1 << 10
+    assert alhr.alhr_tree_int16_levels(c) == 10          # every level of a 2^10 tree
+    c = alhr.Config(batch=1, heads=1, T=1 << 12, d=16, kmax=127, qmax=1, wmax=1)
+    assert alhr.alhr_tree_int16_levels(c) == 8           # 127 * 2^8 = 32512
+    c = alhr.Config(batch=1, heads=1, T=1 << 12, d=16, kmax=0)
+    assert alhr.alhr_tree_int16_levels(c) == 12
+    c.T = 1000
+    assert alhr.alhr_tree_int16_levels(c) == -1

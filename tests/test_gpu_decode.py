@@ -15,6 +15,7 @@ import pytest
 import oracle
 import synth
 from synth.workloads import WORKLOADS, Workload, host_inputs, pair_keys, pair_query_rows, pair_value_rows
+from tree_layout import decode_tree
 
 pytestmark = pytest.mark.gpu
 ATOL = 1e-4
@@ -142,15 +143,19 @@ def test_decode_small_every_step(torch_dev, d, fixed):
     got = run_decode(torch, dev, w, cfg, Kd, Vd, nodes, prefix, Wd, n0, steps, pairs,
                      lambda p: Qh[:, :, p].contiguous(), lambda p: Kh[:, :, p].contiguous(),
                      lambda p: Vh[:, :, p].contiguous())
+    l16 = alhr.alhr_tree_int16_levels(cfg)
     for (b, h) in pairs:
         ref, ref_nodes, ref_pre = decode_oracle_pair(w, b, h, n0, steps, K[b, h], Q[b, h, n0:], W, cfg)
         compare(got[(b, h)], ref)
-        np.testing.assert_array_equal(nodes[b, h, 1:].cpu().numpy(), ref_nodes[1:])
+        np.testing.assert_array_equal(decode_tree(nodes[b, h].cpu().numpy(), l16)[1:],
+                                      ref_nodes[1:])
         np.testing.assert_array_equal(prefix[b, h].cpu().numpy(), ref_pre)
     # after the appends, the tree equals a fresh build of the full keys
     rebuilt = alhr.alhr_build_tree(cfg, Kh)
     torch.cuda.synchronize()
-    assert torch.equal(rebuilt[:, :, 1:], nodes[:, :, 1:])
+    for (b, h) in pairs:
+        np.testing.assert_array_equal(decode_tree(rebuilt[b, h].cpu().numpy(), l16),
+                                      decode_tree(nodes[b, h].cpu().numpy(), l16))
     # and the decode rows equal the prefill rows of the same positions
     full = alhr.alhr_forward(cfg, Qh, Kh, Vh, Wd, fixed_budget=fixed)
     torch.cuda.synchronize()
@@ -191,13 +196,15 @@ def test_decode_full_cache_sampled_pairs(torch_dev):
     import time
     t_replay = time.time()
     W = synth.predictor_weights(w.seed, w.n_classes, d)
+    l16 = alhr.alhr_tree_int16_levels(cfg)
     for (b, h) in pairs:
         K_pair = pair_keys(w, b, h)
         q_rows = pair_query_rows(w, b, h, np.arange(n0, n0 + steps))
         ref, ref_nodes, ref_pre = decode_oracle_pair(w, b, h, n0, steps, K_pair, q_rows, W, cfg)
         compare(got[(b, h)], ref)
         np.testing.assert_array_equal(prefix[b, h].cpu().numpy(), ref_pre)
-        top = nodes[b, h, 1:4096].cpu().numpy()
+        # the top 4095 rows (levels 6..17), int16 and int32 rows both
+        top = decode_tree(nodes[b, h].cpu().numpy(), l16)[1:4096]
         np.testing.assert_array_equal(top, ref_nodes[1:4096])
     say("decode full cache: replayed %d pairs x %d steps in %.1f s" % (len(pairs), steps,
                                                                    time.time() - t_replay))

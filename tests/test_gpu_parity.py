@@ -15,6 +15,7 @@ import pytest
 import oracle
 import synth
 from synth.workloads import WORKLOADS, Workload, host_inputs
+from tree_layout import decode_tree
 
 pytestmark = pytest.mark.gpu
 ATOL = 1e-4
@@ -63,9 +64,11 @@ def check_pair(w, cfg, Q, K, V, W, out, b, h, ts=None, fixed=None):
     return ref
 
 
-def check_nodes(out_nodes, K, b, h):
+def check_nodes(out_nodes, K, b, h, cfg):
+    import learned_tree_routed_amd as alhr
     ref = oracle.build_tree(K[b, h])
-    np.testing.assert_array_equal(out_nodes[b, h][1:], ref[1:])
+    got = decode_tree(out_nodes[b, h], alhr.alhr_tree_int16_levels(cfg))
+    np.testing.assert_array_equal(got[1:], ref[1:])
 
 
 # ------------------------------------------------------------ full parity --
@@ -74,7 +77,7 @@ def test_tiny_every_query(torch_dev):
     w = WORKLOADS["tiny"]
     Q, K, V, W = host_inputs(w)
     out = run_forward(torch, dev, w, Q, K, V, W)
-    check_nodes(out["nodes"], K, 0, 0)
+    check_nodes(out["nodes"], K, 0, 0, w.config())
     check_pair(w, w.config(), Q, K, V, W, out, 0, 0)
 
 
@@ -86,7 +89,7 @@ def test_t1k_every_query(torch_dev):
     cfg = w.config()
     for b in range(w.B):
         for h in range(w.H):
-            check_nodes(out["nodes"], K, b, h)
+            check_nodes(out["nodes"], K, b, h, cfg)
             np.testing.assert_array_equal(out["budget"][b, h], oracle.pair_budgets(Q[b, h], K[b, h], W))
     for b, h in [(0, 0), (3, 5), (7, 7), (5, 2)]:
         check_pair(w, cfg, Q, K, V, W, out, b, h)
@@ -109,7 +112,7 @@ def test_full_size_sampled(torch_dev, name):
     rng = np.random.default_rng(w.seed)
     for b in range(w.B):
         for h in range(w.H):
-            check_nodes(out["nodes"], K, b, h)
+            check_nodes(out["nodes"], K, b, h, cfg)
             np.testing.assert_array_equal(out["budget"][b, h], oracle.pair_budgets(Q[b, h], K[b, h], W))
             check_pair(w, cfg, Q, K, V, W, out, b, h, ts=sample_ts(w.T, rng, 192))
     # every query: size = min(budget, t+1), ascending, own key included, -1 padding
@@ -142,7 +145,11 @@ def test_unfused_path_equals_fused(torch_dev):
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
     assert torch.equal(idx, full["idx"]) and torch.equal(bud, full["budget"])
-    assert torch.equal(nodes[:, :, 1:], full["nodes"][:, :, 1:])
+    l16 = alhr.alhr_tree_int16_levels(cfg)
+    for b in range(2):
+        for h in range(4):
+            np.testing.assert_array_equal(decode_tree(nodes[b, h].cpu().numpy(), l16),
+                                          decode_tree(full["nodes"][b, h].cpu().numpy(), l16))
     assert (O1 - O2).abs().max().item() <= 1e-6
     assert torch.equal(O2, full["O"])
     out = {"budget": bud.cpu().numpy(), "count": cnt.cpu().numpy(), "idx": idx.cpu().numpy(),
@@ -150,14 +157,15 @@ def test_unfused_path_equals_fused(torch_dev):
     check_pair(w, cfg, Q, K, V, W, out, 1, 3)
 
 
-def test_route_stats_match_oracle_counts(torch_dev):
+@pytest.mark.parametrize("name", ["t1k", "t4k"])
+def test_route_stats_match_oracle_counts(torch_dev, name):
     import learned_tree_routed_amd as alhr
     torch, dev = torch_dev
-    w = WORKLOADS["t1k"]
+    w = WORKLOADS[name]
     Q, K, V, W = host_inputs(w, B=1, H=2)
     cfg = w.config(batch=1, heads=2)
     q, k, wt = to_dev(torch, dev, Q, K, W)
-    say("alhr_route_stats t1k B1 H2")
+    say("alhr_route_stats %s B1 H2" % name)
     nodes = alhr.alhr_build_tree(cfg, k)
     bud = alhr.alhr_predict_budget(cfg, q, k, wt)
     idx, cnt, st = alhr.alhr_route_stats(cfg, q, k, nodes, bud)
@@ -165,13 +173,18 @@ def test_route_stats_match_oracle_counts(torch_dev):
     torch.cuda.synchronize()
     assert torch.equal(idx, idx_r)
     st = st.cpu().numpy()
+    L = w.T.bit_length() - 1
+    l16 = alhr.alhr_tree_int16_levels(cfg)
+    assert l16 == min(11, L)   # kmax = 8: 8 * 2^11 = 16384 fits int16, 8 * 2^12 does not
     ref = oracle.pair_forward(Q[0, 1], K[0, 1], V[0, 1], W=W, scale=cfg.scale, with_stats=True)
     for t in range(w.T):
         s = ref["stats"][t]
         # only left children are loaded; the right child's score is derived
-        assert st[0, 1, t, 0] == s["cover_internal"] + s["child_internal"] // 2
-        assert st[0, 1, t, 1] == s["cover_leaf"] + s["child_leaf"] // 2
-        assert st[0, 1, t, 2] == s["neighbours"] and st[0, 1, t, 3] == s["count"]
+        rows = [s["cover_by_level"][l] + s["child_by_level"][l] // 2 for l in range(24)]
+        assert st[0, 1, t, 0] == sum(rows[l16 + 1:])
+        assert st[0, 1, t, 1] == sum(rows[1:l16 + 1])
+        assert st[0, 1, t, 2] == rows[0] == s["cover_leaf"] + s["child_leaf"] // 2
+        assert st[0, 1, t, 3] == s["count"]
 
 
 def test_repeat_runs_are_bit_identical(torch_dev):
@@ -217,7 +230,7 @@ def test_edge_cases_every_query(torch_dev, case):
     out = run_forward(torch, dev, w, Q, K, V, W, cfg=cfg)
     for b in range(2):
         for h in range(2):
-            check_nodes(out["nodes"], K, b, h)
+            check_nodes(out["nodes"], K, b, h, cfg)
             check_pair(w, cfg, Q, K, V, W, out, b, h)
 
 
@@ -257,7 +270,7 @@ def test_wide_int32_path(torch_dev):
     cfg = w.config(kmax=127, qmax=4)
     assert cfg.kmax * (T // 2) >= 1 << 23
     out = run_forward(torch, dev, w, Q, K, V, None, cfg=cfg)
-    check_nodes(out["nodes"], K, 0, 0)
+    check_nodes(out["nodes"], K, 0, 0, cfg)
     ts = sample_ts(T, np.random.default_rng(1), 256)
     check_pair(w, cfg, Q, K, V, None, out, 0, 0, ts=ts)
 
