@@ -87,6 +87,10 @@ def _load():
     lib.alhr_ref_pair_budgets.restype = C.c_int
     lib.alhr_ref_append.argtypes = [i32, i32, i32, P, P, P, P, P, P]
     lib.alhr_ref_append.restype = C.c_int
+    lib.alhr_ref_requant.argtypes = [i64, i32, i32]
+    lib.alhr_ref_requant.restype = i64
+    lib.alhr_ref_split_qk.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P]
+    lib.alhr_ref_split_qk.restype = C.c_int
     _lib = lib
     return lib
 
@@ -230,3 +234,24 @@ def append(p, k_new, v_new, K, V, nodes, prefix_row):
                                  _p(prefix_row))
     if rc:
         raise ValueError("alhr_ref_append failed: %d" % rc)
+
+
+def requant(acc, shift, clamp):
+    """The splitter's requantisation of one int64 accumulator."""
+    return int(_load().alhr_ref_requant(int(acc), int(shift), int(clamp)))
+
+
+def split_qk(X, W, heads, d, shift, qclamp, kclamp):
+    """Query/key splitter: X int8 [batch, T, d_model], W int8
+    [2*heads*d, d_model] -> (Q, K) int8 [batch, heads, T, d]."""
+    X = _c(X, np.int8)
+    W = _c(W, np.int8)
+    batch, T, d_model = X.shape
+    assert W.shape == (2 * heads * d, d_model)
+    Q = np.zeros((batch, heads, T, d), dtype=np.int8)
+    K = np.zeros((batch, heads, T, d), dtype=np.int8)
+    rc = _load().alhr_ref_split_qk(batch, heads, T, d, d_model, shift, qclamp, kclamp,
+                                   _p(X), _p(W), _p(Q), _p(K))
+    if rc:
+        raise ValueError("alhr_ref_split_qk failed: %d" % rc)
+    return Q, K

@@ -23,6 +23,10 @@
  *   - plain dot-product softmax attention over the keys found:
  *     README "Inference stage".
  *   - decode, one token at a time: news, section "ALHR是什么".
+ *   - the query/key splitter that turns the layer input into queries and
+ *     keys before the tree is built, one of the two trained functions:
+ *     README "Inference stage" (first paragraph) and "Training stage"
+ *     (last paragraph).
  *
  * Readings where the pages leave a step open (each listed with its reason
  * in the design notes): positional leaves; node value = raw sum; branch
@@ -32,7 +36,10 @@
  * neighbours = the window t, t-1, ... taken unconditionally; the descent
  * covers [0, t+1-n) with maximal complete subtrees and runs a beam of width
  * r = C - n in which every internal node expands each round and leaves stay
- * and compete; order = score descending, then start position ascending.
+ * and compete; order = score descending, then start position ascending;
+ * the splitter = two bias-free linear maps of each token's input row (one
+ * for the queries, one for the keys, heads side by side), requantised to
+ * int8 by a rounding right shift and a symmetric clamp.
  *
  * Arithmetic.  Every integer quantity (node sums, prefix sums, scores,
  * predictor logits) is an exact int64.  Attention logits, softmax and the
@@ -398,5 +405,64 @@ int alhr_ref_pair_budgets(int32_t T, int32_t d, const int8_t *Q, const int8_t *K
         if (b < 1) return REF_ERR_ARG;
         budget[t] = b;
     }
+    return REF_OK;
+}
+
+/* ---------------------------------------------------------------------
+ * Query/key splitter (README "Inference stage": the layer input is split
+ * into queries and keys, then the tree is built over the keys; "Training
+ * stage": the splitter is trained with the budget predictor).  The pages
+ * give no formula; the reading here is the usual per-token projection:
+ *   acc_o(b, t) = sum_i X[b][t][i] * W[o][i]            (exact int64)
+ * for output feature o < 2*heads*d, where rows o = h*d + j of W give query
+ * feature j of head h and rows heads*d + h*d + j give key feature j of head
+ * h.  Each accumulator is requantised to int8 by
+ *   requant(acc) = clamp(floor((acc + half) / 2^shift), -c, c),
+ *   half = 2^(shift-1) for shift >= 1, 0 for shift = 0,
+ * i.e. round half up, with c = qclamp for queries and kclamp for keys.
+ * X is int8 [batch][T][d_model]; W int8 [2*heads*d][d_model]; Q and K are
+ * written as int8 [batch][heads][T][d].
+ * --------------------------------------------------------------------- */
+static int64_t floor_div_pow2(int64_t a, int shift)
+{
+    const int64_t m = (int64_t)1 << shift;
+    int64_t q = a / m;                   /* truncates toward zero */
+    if (a % m != 0 && a < 0) q -= 1;     /* step down to the floor */
+    return q;
+}
+
+int64_t alhr_ref_requant(int64_t acc, int32_t shift, int32_t clamp)
+{
+    const int64_t half = shift >= 1 ? ((int64_t)1 << (shift - 1)) : 0;
+    int64_t v = floor_div_pow2(acc + half, shift);
+    if (v > clamp) v = clamp;
+    if (v < -clamp) v = -clamp;
+    return v;
+}
+
+int alhr_ref_split_qk(int32_t batch, int32_t heads, int32_t T, int32_t d,
+                      int32_t d_model, int32_t shift, int32_t qclamp,
+                      int32_t kclamp, const int8_t *X, const int8_t *W,
+                      int8_t *Q, int8_t *K)
+{
+    if (batch < 1 || heads < 1 || T < 1 || d < 1 || d_model < 1 || shift < 0 ||
+        shift > 30 || qclamp < 1 || qclamp > 127 || kclamp < 1 || kclamp > 127)
+        return REF_ERR_ARG;
+    const int64_t HD = (int64_t)heads * d;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t t = 0; t < T; ++t) {
+            const int8_t *x = X + (b * T + t) * d_model;
+            for (int64_t o = 0; o < 2 * HD; ++o) {
+                const int8_t *w = W + o * d_model;
+                int64_t acc = 0;
+                for (int64_t i = 0; i < d_model; ++i) acc += (int64_t)x[i] * w[i];
+                const int is_key = o >= HD;
+                const int64_t f = is_key ? o - HD : o;   /* h*d + j */
+                const int64_t h = f / d, j = f % d;
+                const int64_t dst = ((b * heads + h) * T + t) * d + j;
+                const int64_t v = alhr_ref_requant(acc, shift, is_key ? kclamp : qclamp);
+                if (is_key) K[dst] = (int8_t)v; else Q[dst] = (int8_t)v;
+            }
+        }
     return REF_OK;
 }

@@ -384,3 +384,94 @@ def test_dense_mode_keys_per_token_matches_printed_table():
         else:
             # the page prints the causal mean (T+1)/2 rounded down
             assert abs((T + 1) / 2 - printed) <= 0.5
+
+
+# ------------------------------------------------------------- splitter --
+# The pages give the splitter no formula; the reading is a per-token
+# bias-free projection requantised by round-half-up shift and clamp.  These
+# pins fix that definition by hand-worked values and by special inputs whose
+# outputs are known without the oracle's own loops.
+
+@pytest.mark.parametrize("acc,shift,clamp,expected", [
+    (5, 2, 127, 1),       # (5 + 2) / 4 = 1.75 -> 1
+    (6, 2, 127, 2),       # 8 / 4 = 2
+    (2, 2, 127, 1),       # 0.5 rounds up: (2 + 2) / 4 = 1
+    (-2, 2, 127, 0),      # -0.5 rounds up: (-2 + 2) / 4 = 0
+    (-6, 2, 127, -1),     # -1.5 rounds up: -4 / 4 = -1
+    (-7, 2, 127, -2),     # -1.75: floor(-5 / 4) = -2
+    (-10, 2, 127, -2),    # -8 / 4 = -2
+    (1000, 3, 9, 9),      # 125.5 -> 125 -> clamp 9
+    (-1000, 3, 9, -9),    # -125 -> clamp -9
+    (-3, 0, 127, -3),     # shift 0 is the identity before the clamp
+    (200, 0, 127, 127),
+    (-200, 0, 127, -127),
+    ((1 << 31) + 5, 1, 127, 127),
+    (63, 6, 127, 1),      # 63 / 64 = 0.98 -> (63 + 32) / 64 = 1.48 -> 1
+    (31, 6, 127, 0),      # 0.48 -> (31 + 32) / 64 = 0.98 -> 0
+    (-32, 6, 127, 0),     # -0.5 rounds up to 0
+    (-33, 6, 127, -1),    # -0.52 -> floor(-1 / 64) = -1
+])
+def test_requant_rounds_half_up_and_clamps(acc, shift, clamp, expected):
+    assert oracle.requant(acc, shift, clamp) == expected
+
+
+def test_split_one_hot_rows_pick_weight_columns():
+    """A token whose input row is v * e_i gets requant(v * W[o, i]) in
+    output feature o; a transposed or mis-strided W fails this."""
+    rng = np.random.default_rng(21)
+    batch, T, heads, d, dm = 2, 8, 3, 16, 40
+    W = rng.integers(-5, 6, size=(2 * heads * d, dm)).astype(np.int8)
+    X = np.zeros((batch, T, dm), np.int8)
+    picks = {}
+    for b in range(batch):
+        for t in range(T):
+            i, v = int(rng.integers(0, dm)), int(rng.integers(-20, 21))
+            X[b, t, i] = v
+            picks[b, t] = (i, v)
+    Q, K = oracle.split_qk(X, W, heads, d, shift=1, qclamp=30, kclamp=20)
+    for (b, t), (i, v) in picks.items():
+        for h in range(heads):
+            for j in range(d):
+                o = h * d + j
+                assert Q[b, h, t, j] == oracle.requant(v * int(W[o, i]), 1, 30)
+                assert K[b, h, t, j] == oracle.requant(v * int(W[heads * d + o, i]), 1, 20)
+
+
+def test_split_selector_weights_route_features_to_heads():
+    """W_Q = 2 x (a permuted identity), W_K = -2 x identity and shift 1 give
+    Q[b, h, t, j] = X[b, t, perm(h*d + j)] and K = -X exactly."""
+    rng = np.random.default_rng(22)
+    batch, T, heads, d = 2, 16, 4, 16
+    dm = heads * d
+    perm = (np.arange(dm) * 5 + 3) % dm          # 5 is prime to 64: a permutation
+    W = np.zeros((2 * dm, dm), np.int8)
+    W[np.arange(dm), perm] = 2
+    W[dm + np.arange(dm), np.arange(dm)] = -2
+    X = rng.integers(-60, 61, size=(batch, T, dm)).astype(np.int8)
+    Q, K = oracle.split_qk(X, W, heads, d, shift=1, qclamp=127, kclamp=127)
+    for h in range(heads):
+        for j in range(d):
+            np.testing.assert_array_equal(Q[:, h, :, j], X[:, :, perm[h * d + j]])
+            np.testing.assert_array_equal(K[:, h, :, j], -X[:, :, h * d + j])
+
+
+def test_split_is_linear_and_scale_exact_without_rounding():
+    """With shift 0 and no saturation the map is linear in X; scaling X by
+    2^s and shifting by s reproduces the unshifted result exactly."""
+    rng = np.random.default_rng(23)
+    batch, T, heads, d, dm = 1, 8, 2, 16, 24
+    W = rng.integers(-3, 4, size=(2 * heads * d, dm)).astype(np.int8)
+    X1 = rng.integers(-2, 3, size=(batch, T, dm)).astype(np.int8)
+    X2 = rng.integers(-2, 3, size=(batch, T, dm)).astype(np.int8)
+    q1, k1 = oracle.split_qk(X1, W, heads, d, 0, 127, 127)
+    q2, k2 = oracle.split_qk(X2, W, heads, d, 0, 127, 127)
+    q12, k12 = oracle.split_qk(X1 + X2, W, heads, d, 0, 127, 127)
+    np.testing.assert_array_equal(q12.astype(int), q1.astype(int) + q2.astype(int))
+    np.testing.assert_array_equal(k12.astype(int), k1.astype(int) + k2.astype(int))
+    qs, ks = oracle.split_qk((X1 * 16).astype(np.int8), W, heads, d, 4, 127, 127)
+    np.testing.assert_array_equal(qs, q1)
+    np.testing.assert_array_equal(ks, k1)
+    # tokens are independent: reversing them reverses the outputs
+    qr, kr = oracle.split_qk(X1[:, ::-1], W, heads, d, 0, 127, 127)
+    np.testing.assert_array_equal(qr, q1[:, :, ::-1])
+    np.testing.assert_array_equal(kr, k1[:, :, ::-1])
