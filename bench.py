@@ -37,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "route_attend_t16k_counters.txt")
 ROUTE_SOURCES = [os.path.join(ROOT, "learned_tree_routed_amd", "csrc", f)
                  for f in ("route.hip", "device.h")]
@@ -104,6 +105,45 @@ def cpu_baseline(w, Q, K, V, W, stride):
                       % (w.name, stride, w.B * w.H, n, dt)}
 
 
+def bench_splitter(alhr, torch, dev, w, reps=20):
+    """Time alhr_split_qk on seeded input rows: batch x T tokens of d_model =
+    heads * d int8 features projected to the workload's Q and K."""
+    import synth
+    dm = w.H * w.d
+    X = torch.from_numpy(synth.split_inputs(w.seed, w.B, dm, 0, w.T)).to(dev)
+    Wsp = torch.from_numpy(synth.split_weights(w.seed, w.H, w.d, dm)).to(dev)
+    scfg = alhr.SplitConfig(batch=w.B, heads=w.H, T=w.T, d=w.d, d_model=dm, shift=6,
+                            qclamp=9, kclamp=8)
+    Qs, Ks = alhr.alhr_split_qk(scfg, X, Wsp)
+    torch.cuda.synchronize()
+    # one launch takes about as long as the host needs to submit one, so the
+    # launches are captured in a HIP graph (reps per replay) and the events
+    # bracket whole replays: the per-launch time is then the GPU's alone
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            alhr.alhr_split_qk(scfg, X, Wsp, Qs, Ks)
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    for e in ev:
+        e[0].record()
+        g.replay()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / reps
+    M, N = w.B * w.T, 2 * w.H * w.d
+    ops = 2 * M * N * dm
+    nbytes = M * dm + N * dm + M * N
+    tops = ops / (ms * 1e-3) / 1e12
+    return {"kernel": "k_split (int8 MFMA 32x32x32, 128x128 tiles)",
+            "shape": {"tokens": M, "d_model": dm, "outputs": N},
+            "ms": ms, "ops_per_launch": ops, "bytes_per_launch": nbytes,
+            "roofline": {"bound": "mfma", "achieved": tops, "peak": INT8_MFMA_PEAK_TOPS,
+                         "unit": "TOP/s", "frac": tops / INT8_MFMA_PEAK_TOPS},
+            "hbm_GBps": nbytes / (ms * 1e-3) / 1e9}
+
+
 def bench_prefill(args, torch, dev):
     import learned_tree_routed_amd as alhr
     from synth.workloads import WORKLOADS, host_inputs
@@ -164,6 +204,10 @@ def bench_prefill(args, torch, dev):
         dense_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev]))
         del Od
 
+    # the query/key splitter at this workload's shapes (d_model = heads * d),
+    # timed on its own: it precedes the tree path and is not part of a step
+    splitter = bench_splitter(alhr, torch, dev, w)
+
     # load counts of the routing (untimed), for the byte model
     _, _, st = alhr.alhr_route_stats(cfg, q, k, nodes, budget if wt is not None else None, fixed)
     torch.cuda.synchronize()
@@ -195,6 +239,7 @@ def bench_prefill(args, torch, dev):
         "dense_baseline": None if dense_ms is None else {
             "kernel": "alhr_dense_attend (causal, int8 MFMA scores, fp32 MFMA values)",
             "ms": dense_ms, "routed_step_speedup": dense_ms / ms_step},
+        "splitter": splitter,
         "diagnostics": {"mean_budget": float(bud.mean()), "mean_keys_per_query": float(cnt.mean()),
                         "mean_tree_rows_loaded_int32": float(stats[..., 0].mean()),
                         "mean_tree_rows_loaded_int16": float(stats[..., 1].mean()),

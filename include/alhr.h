@@ -224,6 +224,39 @@ alhr_status alhr_dense_attend(const alhr_config *cfg, const int8_t *Q,
                               const int8_t *K, const float *V, float *O,
                               void *stream);
 
+/* Query/key splitter: the step before the tree that turns the layer input
+ * into queries and keys (README "Inference stage", first paragraph; the
+ * splitter is one of the two trained functions, README "Training stage").
+ * The pages give no formula; the function computed is, for every token
+ * m = b*T + t and output feature o < 2*heads*d,
+ *   acc = sum_i X[m][i] * W[o][i]                 (exact int32)
+ *   v   = clamp(floor((acc + half) / 2^shift), -c, c)
+ * with half = 2^(shift-1) (0 when shift = 0), i.e. round half up, and
+ * c = qclamp for o < heads*d, kclamp otherwise.  Feature o = h*d + j is
+ * written to Q[b][h][t][j]; feature heads*d + h*d + j to K[b][h][t][j].
+ *   X  int8 [batch, T, d_model]         input rows
+ *   W  int8 [2 * heads * d, d_model]    weight rows, queries then keys
+ *   Q, K int8 [batch, heads, T, d]      outputs (the layout of the tree path)
+ * Checks: batch, heads >= 1; 1 <= T <= 2^20; d in {16, 32, 64, 128, 256};
+ * d_model a multiple of 16 in [16, 16384] (so |acc| < 2^31 for any int8
+ * input); 0 <= shift <= 30; 1 <= qclamp, kclamp <= 127; batch * T *
+ * max(d_model, heads * d) < 2^31; pointers non-NULL and 16-byte aligned.
+ * The outputs satisfy |Q| <= qclamp and |K| <= kclamp, the bounds to declare
+ * as qmax / kmax in the alhr_config of the tree path. */
+typedef struct alhr_split_config {
+    int32_t batch;
+    int32_t heads;
+    int32_t T;
+    int32_t d;          /* head dimension of Q and K                          */
+    int32_t d_model;    /* input row length                                   */
+    int32_t shift;      /* requantisation right shift                         */
+    int32_t qclamp;     /* |Q| <= qclamp                                      */
+    int32_t kclamp;     /* |K| <= kclamp                                      */
+} alhr_split_config;
+
+alhr_status alhr_split_qk(const alhr_split_config *cfg, const int8_t *X,
+                          const int8_t *W, int8_t *Q, int8_t *K, void *stream);
+
 /* Static text for a status code. */
 const char *alhr_status_string(alhr_status status);
 

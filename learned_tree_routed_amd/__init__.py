@@ -24,7 +24,7 @@ __all__ = [
     "alhr_route_stats", "alhr_sparse_attend", "alhr_route_attend", "alhr_forward",
     "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_dense_attend",
     "alhr_status_string", "alhr_last_error", "alhr_version", "alhr_tree_int16_levels",
-    "EXPORTED",
+    "alhr_split_qk", "SplitConfig", "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +36,7 @@ EXPORTED = (
     "alhr_route_stats", "alhr_sparse_attend", "alhr_route_attend", "alhr_forward",
     "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_dense_attend",
     "alhr_status_string", "alhr_last_error", "alhr_version", "alhr_tree_int16_levels",
+    "alhr_split_qk",
 )
 
 STATUS = {0: "ALHR_OK", -1: "ALHR_ERR_ARG", -2: "ALHR_ERR_OVERFLOW", -3: "ALHR_ERR_DEVICE",
@@ -87,6 +88,32 @@ class Config:
         return cc
 
 
+class CSplitConfig(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("batch", "heads", "T", "d", "d_model", "shift",
+                                         "qclamp", "kclamp")]
+
+
+@dataclasses.dataclass
+class SplitConfig:
+    """Mirror of ``alhr_split_config``: the query/key splitter's shapes and
+    its requantisation (round-half-up right shift, then symmetric clamps that
+    become the tree path's qmax / kmax)."""
+    batch: int
+    heads: int
+    T: int
+    d: int
+    d_model: int
+    shift: int
+    qclamp: int = 9
+    kclamp: int = 8
+
+    def c(self):
+        cc = CSplitConfig()
+        for f in CSplitConfig._fields_:
+            setattr(cc, f[0], getattr(self, f[0]))
+        return cc
+
+
 _lib = None
 
 
@@ -122,6 +149,7 @@ def load():
         "alhr_last_error": ([], C.c_char_p),
         "alhr_version": ([], i32),
         "alhr_tree_int16_levels": ([cfgp], i32),
+        "alhr_split_qk": ([C.POINTER(CSplitConfig), P, P, P, P, P], C.c_int),
     }
     for name, (args, res) in sigs.items():
         f = getattr(lib, name)
@@ -365,6 +393,19 @@ def alhr_decode_step(cfg, pos, q_new, K, V, nodes, prefix, W=None, fixed_budget=
           _ptr(nodes), _ptr(prefix), _ptr(W), int(fixed_budget), _ptr(budget), _ptr(idx),
           _ptr(count), _ptr(O), _stream(stream))
     return idx, count, O
+
+
+def alhr_split_qk(scfg, X, W, Q=None, K=None, stream=None):
+    """Query/key splitter: X int8 [batch, T, d_model] and W int8
+    [2 * heads * d, d_model] -> (Q, K) int8 [batch, heads, T, d]."""
+    torch = _torch()
+    _check("X", X, torch.int8, (scfg.batch, scfg.T, scfg.d_model))
+    _check("W", W, torch.int8, (2 * scfg.heads * scfg.d, scfg.d_model), X.device)
+    rows = (scfg.batch, scfg.heads, scfg.T, scfg.d)
+    Q = _out(Q, "Q", torch.int8, rows, X.device)
+    K = _out(K, "K", torch.int8, rows, X.device)
+    _call("alhr_split_qk", C.byref(scfg.c()), _ptr(X), _ptr(W), _ptr(Q), _ptr(K), _stream(stream))
+    return Q, K
 
 
 def alhr_dense_attend(cfg, Q, K, V, O=None, stream=None):

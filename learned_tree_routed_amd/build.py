@@ -30,7 +30,8 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
 ]
 
-SOURCES = ["api.hip", "build.hip", "predict.hip", "route.hip", "decode.hip", "dense.hip"]
+SOURCES = ["api.hip", "build.hip", "predict.hip", "route.hip", "decode.hip", "dense.hip",
+           "split.hip"]
 
 
 def _run(cmd):

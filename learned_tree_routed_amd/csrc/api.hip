@@ -1,6 +1,7 @@
 // C ABI of libalhr: argument validation on the host, then kernel launches on
 // the caller's stream.  Every check runs before the first HIP call, so a
 // rejected call touches neither the device nor the outputs.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -313,6 +314,36 @@ alhr_status alhr_dense_attend(const alhr_config* cfg, const int8_t* Q, const int
     ALHR_NEED_PTR(O);
     (void)hipGetLastError();
     return device_status(fn, alhr::launch_dense(s, Q, K, V, O, as_stream(stream)));
+}
+
+alhr_status alhr_split_qk(const alhr_split_config* cfg, const int8_t* X, const int8_t* W,
+                          int8_t* Q, int8_t* K, void* stream)
+{
+    const char* fn = "alhr_split_qk";
+    if (!cfg) return fail(ALHR_ERR_ARG, "%s: cfg is NULL", fn);
+    const alhr_split_config& c = *cfg;
+    if (c.batch < 1 || c.heads < 1)
+        return fail(ALHR_ERR_ARG, "%s: batch = %d and heads = %d must be >= 1", fn, c.batch, c.heads);
+    if (c.T < 1 || c.T > (1 << 20)) return fail(ALHR_ERR_ARG, "%s: T = %d outside [1, 2^20]", fn, c.T);
+    if (c.d != 16 && c.d != 32 && c.d != 64 && c.d != 128 && c.d != 256)
+        return fail(ALHR_ERR_UNSUPPORTED, "%s: d = %d is not built (16, 32, 64, 128, 256)", fn, c.d);
+    if (c.d_model < 16 || c.d_model > 16384 || c.d_model % 16)
+        return fail(ALHR_ERR_ARG, "%s: d_model = %d must be a multiple of 16 in [16, 16384]", fn,
+                    c.d_model);
+    if (c.shift < 0 || c.shift > 30) return fail(ALHR_ERR_ARG, "%s: shift = %d outside [0, 30]", fn, c.shift);
+    if (c.qclamp < 1 || c.qclamp > 127 || c.kclamp < 1 || c.kclamp > 127)
+        return fail(ALHR_ERR_ARG, "%s: qclamp = %d, kclamp = %d must be in [1, 127]", fn, c.qclamp,
+                    c.kclamp);
+    const int64_t wide = std::max<int64_t>(c.d_model, (int64_t)c.heads * c.d);
+    if ((int64_t)c.batch * c.T * wide >= ((int64_t)1 << 31))
+        return fail(ALHR_ERR_ARG, "%s: batch * T * max(d_model, heads * d) must stay below 2^31", fn);
+    ALHR_NEED_PTR(X);
+    ALHR_NEED_PTR(W);
+    ALHR_NEED_PTR(Q);
+    ALHR_NEED_PTR(K);
+    const alhr::SplitShape s{c.batch, c.heads, c.T, c.d, c.d_model, c.shift, c.qclamp, c.kclamp};
+    (void)hipGetLastError();
+    return device_status(fn, alhr::launch_split(s, X, W, Q, K, as_stream(stream)));
 }
 
 alhr_status alhr_prefix_from_tree(const alhr_config* cfg, int32_t n, const int8_t* K,

@@ -51,4 +51,11 @@ hipError_t launch_decode(const Shape& s, int pos, const int8_t* q_new, const int
 hipError_t launch_dense(const Shape& s, const int8_t* Q, const int8_t* K, const float* V, float* O,
                         hipStream_t st);
 
+struct SplitShape {
+    int batch, heads, T, d, d_model, shift, qclamp, kclamp;
+};
+
+hipError_t launch_split(const SplitShape& s, const int8_t* X, const int8_t* W, int8_t* Q,
+                        int8_t* K, hipStream_t st);
+
 }  // namespace alhr

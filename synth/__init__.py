@@ -26,7 +26,9 @@ predictor weights are uniform in [-4, 4].  The tiny configuration instead
 draws Q and K uniformly in [-4, 4].
 
 Streams: 0 centres, 1 cluster id, 2 key noise, 3 query source, 4 query noise,
-5 values, 6 predictor weights, 7 uniform queries, 8 uniform keys.
+5 values, 6 predictor weights, 7 uniform queries, 8 uniform keys, 10 the
+query/key splitter's input rows (b, t, feature i), 11 the splitter's weights
+(t := output feature o, i := input feature).
 """
 from __future__ import annotations
 
@@ -35,7 +37,7 @@ import numpy as np
 __all__ = [
     "mix64", "pack_key", "uniform_int",
     "clustered_keys", "copied_queries", "values", "predictor_weights",
-    "uniform_i8", "query_sources",
+    "uniform_i8", "query_sources", "split_inputs", "split_weights", "STREAM_X", "STREAM_WS",
     "STREAM_CENTRE", "STREAM_CLUSTER", "STREAM_KNOISE", "STREAM_SRC",
     "STREAM_QNOISE", "STREAM_V", "STREAM_W", "STREAM_UQ", "STREAM_UK",
     "N_CENTRES",
@@ -44,6 +46,7 @@ __all__ = [
 STREAM_CENTRE, STREAM_CLUSTER, STREAM_KNOISE = 0, 1, 2
 STREAM_SRC, STREAM_QNOISE, STREAM_V, STREAM_W = 3, 4, 5, 6
 STREAM_UQ, STREAM_UK = 7, 8
+STREAM_X, STREAM_WS = 10, 11
 N_CENTRES = 64
 
 _U64 = np.uint64
@@ -157,3 +160,23 @@ def uniform_i8(seed, stream, lo, hi, B, H, d, t0, nt):
     _check(B, H, t0, nt, d)
     b, h, t, i = _grid(B, H, t0, nt, d)
     return uniform_int(mix64(pack_key(seed, stream, b, h, t, i)), lo, hi).astype(np.int8)
+
+
+def split_inputs(seed, batch, d_model, t0, nt, lo=-8, hi=8):
+    """Splitter input rows, int8 [batch, nt, d_model] uniform in [lo, hi]
+    (positions t0 .. t0 + nt - 1)."""
+    assert 0 <= t0 and t0 + nt <= (1 << 20) and d_model <= (1 << 16) and batch <= 256
+    b = np.arange(batch, dtype=np.int64)[:, None, None]
+    t = np.arange(t0, t0 + nt, dtype=np.int64)[None, :, None]
+    i = np.arange(d_model, dtype=np.int64)[None, None, :]
+    return uniform_int(mix64(pack_key(seed, STREAM_X, b, 0, t, i)), lo, hi).astype(np.int8)
+
+
+def split_weights(seed, heads, d, d_model, lo=-4, hi=4):
+    """Splitter weights, int8 [2 * heads * d, d_model] uniform in [lo, hi]
+    (rows: query features of every head, then key features)."""
+    n = 2 * heads * d
+    assert n <= (1 << 20) and d_model <= (1 << 16)
+    o = np.arange(n, dtype=np.int64)[:, None]
+    i = np.arange(d_model, dtype=np.int64)[None, :]
+    return uniform_int(mix64(pack_key(seed, STREAM_WS, 0, 0, o, i)), lo, hi).astype(np.int8)

@@ -203,3 +203,49 @@ def test_int16_tree_levels_follow_the_key_bound():
     assert alhr.alhr_tree_int16_levels(c) == 12
     c.T = 1000
     assert alhr.alhr_tree_int16_levels(c) == -1
+
+
+def split_call(**over):
+    c = alhr.SplitConfig(batch=1, heads=8, T=16384, d=64, d_model=512, shift=6)
+    ptrs = dict(X=P0, W=P0, Q=P0, K=P0)
+    for k, v in over.items():
+        if k in ptrs:
+            ptrs[k] = v
+        else:
+            setattr(c, k, v)
+    return status("alhr_split_qk", C.byref(c.c()), ptrs["X"], ptrs["W"], ptrs["Q"], ptrs["K"], NULL)
+
+
+@pytestmark_cpu
+@pytest.mark.parametrize("over,code,frag", [
+    ({"batch": 0}, -1, "batch"),
+    ({"heads": 0}, -1, "heads"),
+    ({"T": 0}, -1, "T = 0"),
+    ({"T": (1 << 20) + 1}, -1, "outside"),
+    ({"d": 48}, -4, "not built"),
+    ({"d_model": 8}, -1, "d_model"),
+    ({"d_model": 520}, -1, "multiple of 16"),
+    ({"d_model": 16400}, -1, "d_model"),
+    ({"shift": -1}, -1, "shift"),
+    ({"shift": 31}, -1, "shift"),
+    ({"qclamp": 0}, -1, "qclamp"),
+    ({"kclamp": 128}, -1, "kclamp"),
+    ({"batch": 64, "T": 1 << 20, "d_model": 64}, -1, "2^31"),
+    ({"X": NULL}, -1, "'X'"),
+    ({"K": P_ODD}, -1, "aligned"),
+])
+def test_split_config_rejected_before_launch(over, code, frag):
+    st, msg = split_call(**over)
+    assert st == code, msg
+    assert frag in msg, msg
+
+
+def test_split_binding_checks_shapes_before_the_library():
+    torch = pytest.importorskip("torch")
+    s = alhr.SplitConfig(batch=1, heads=2, T=16, d=16, d_model=32, shift=3)
+    with pytest.raises(ValueError):
+        alhr.alhr_split_qk(s, torch.zeros((1, 16, 48), dtype=torch.int8),
+                           torch.zeros((64, 32), dtype=torch.int8))
+    with pytest.raises(TypeError):
+        alhr.alhr_split_qk(s, torch.zeros((1, 16, 32), dtype=torch.float32),
+                           torch.zeros((64, 32), dtype=torch.int8))

@@ -43,3 +43,19 @@ def test_single_pair_helpers_equal_batched_draws():
         rows = np.array([0, 1, 77, 299])
         np.testing.assert_array_equal(pair_query_rows(w, b, h, rows), Q[b, h, rows])
         np.testing.assert_array_equal(pair_value_rows(w, b, h, rows), V[b, h, rows])
+
+
+def test_split_generators_are_slices_of_one_stream():
+    """Splitter inputs and weights are pure functions of their counters:
+    any slice regenerates identically, and distinct seeds differ."""
+    import numpy as np
+    import synth
+    X = synth.split_inputs(4, 2, 48, 0, 40)
+    np.testing.assert_array_equal(synth.split_inputs(4, 2, 48, 10, 20), X[:, 10:30])
+    assert X.min() >= -8 and X.max() <= 8 and X.dtype == np.int8
+    Wsp = synth.split_weights(4, 3, 16, 48)
+    assert Wsp.shape == (96, 48) and Wsp.min() >= -4 and Wsp.max() <= 4
+    assert not np.array_equal(Wsp, synth.split_weights(5, 3, 16, 48))
+    # both values of each extreme occur in a large draw
+    big = synth.split_inputs(4, 1, 1024, 0, 64, lo=-128, hi=127)
+    assert big.min() == -128 and big.max() == 127
