@@ -166,6 +166,25 @@ __device__ __forceinline__ int score_node(const int32_t* __restrict__ nodes_pair
     return group_sum<LPR>(acc);
 }
 
+// Largest x in [0, span] with at least `need` values rel >= x over the wave
+// (NS values per lane; zeros never count for x >= 1, and x = 0 is returned
+// when no x >= 1 qualifies).  Bits are decided from the most significant
+// down: x | bit is kept when enough values reach it.  Wave-uniform.
+template <int NS>
+__device__ __forceinline__ uint32_t bit_search(const uint32_t (&rel)[NS], uint32_t span, int need)
+{
+    uint32_t x = 0u;
+    for (uint32_t bit = span ? 0x80000000u >> __builtin_clz(span) : 0u; bit; bit >>= 1) {
+        const uint32_t c = x | bit;
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) cnt += wave_count(rel[j] >= c);
+        x = cnt >= need ? c : x;
+        x = uniform(x);
+    }
+    return x;
+}
+
 // Keep the best min(r, #non-empty) keys of cand[0, n) (0 = empty slot) in
 // beam[0, ...), in slot order, and return how many were kept; `inner` tells
 // whether any kept node is internal.  NS slots per lane (n <= 64 * NS).
@@ -199,18 +218,13 @@ __device__ int select_best_ns(const uint64_t* cand, int n, int r, uint64_t* beam
         }
         mx = wave_max_u32(mx);
         mn = wave_min_u32(mn);
-        // largest threshold with at least r scores >= it (scalar loop)
-        uint32_t lo = uniform(mn), hb = uniform(mx);
-        while (lo < hb) {
-            const uint32_t mid = lo + ((hb - lo + 1u) >> 1);
-            int c = 0;
+        // largest threshold with at least r scores >= it: a bitwise search,
+        // most significant bit first, over the scores relative to the minimum
+        // (empty slots read 0 and never reach a candidate threshold >= 1)
+        uint32_t rel[NS];
 #pragma unroll
-            for (int j = 0; j < NS; ++j) c += wave_count(h[j] >= mid);
-            if (c >= r) lo = mid;
-            else hb = mid - 1u;
-            lo = uniform(lo);
-            hb = uniform(hb);
-        }
+        for (int j = 0; j < NS; ++j) rel[j] = k[j] != 0ull ? h[j] - mn : 0u;
+        const uint32_t lo = uniform(mn) + bit_search<NS>(rel, uniform(mx) - uniform(mn), r);
         int gt = 0, eq = 0;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
@@ -237,17 +251,10 @@ __device__ int select_best_ns(const uint64_t* cand, int n, int r, uint64_t* beam
             }
             lmx = wave_max_u32(lmx);
             lmn = wave_min_u32(lmn);
-            uint32_t a = uniform(lmn), bb = uniform(lmx);
-            while (a < bb) {
-                const uint32_t mid = a + ((bb - a + 1u) >> 1);
-                int c = 0;
+            uint32_t lrel[NS];
 #pragma unroll
-                for (int j = 0; j < NS; ++j) c += wave_count(tie[j] && l[j] >= mid);
-                if (c >= need) a = mid;
-                else bb = mid - 1u;
-                a = uniform(a);
-                bb = uniform(bb);
-            }
+            for (int j = 0; j < NS; ++j) lrel[j] = tie[j] ? l[j] - lmn : 0u;
+            const uint32_t a = uniform(lmn) + bit_search<NS>(lrel, uniform(lmx) - uniform(lmn), need);
 #pragma unroll
             for (int j = 0; j < NS; ++j)
                 sel[j] = (k[j] != 0ull && h[j] > lo) || (tie[j] && l[j] >= a);
