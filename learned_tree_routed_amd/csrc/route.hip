@@ -166,10 +166,13 @@ __device__ __forceinline__ int score_node(const int32_t* __restrict__ nodes_pair
     return group_sum<LPR>(acc);
 }
 
-// Largest x in [0, span] with at least `need` values rel >= x over the wave
-// (NS values per lane; zeros never count for x >= 1, and x = 0 is returned
-// when no x >= 1 qualifies).  Bits are decided from the most significant
-// down: x | bit is kept when enough values reach it.  Wave-uniform.
+// A threshold x in [0, span] that selects the `need` largest values rel over
+// the wave (NS values per lane; zeros never count for x >= 1): bits are
+// decided from the most significant down, x | bit being kept when at least
+// `need` values reach it.  The search stops early once exactly `need` values
+// reach x, since {rel >= x} is then the answer; otherwise it ends at the
+// largest x with at least `need` values >= x (ties at x are the caller's).
+// x = 0 is returned when no x >= 1 qualifies.  Wave-uniform.
 template <int NS>
 __device__ __forceinline__ uint32_t bit_search(const uint32_t (&rel)[NS], uint32_t span, int need)
 {
@@ -179,8 +182,9 @@ __device__ __forceinline__ uint32_t bit_search(const uint32_t (&rel)[NS], uint32
         int cnt = 0;
 #pragma unroll
         for (int j = 0; j < NS; ++j) cnt += wave_count(rel[j] >= c);
-        x = cnt >= need ? c : x;
+        if (cnt >= need) x = c;
         x = uniform(x);
+        if (cnt == need) break;
     }
     return x;
 }
