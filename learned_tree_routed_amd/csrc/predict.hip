@@ -30,9 +30,16 @@ __device__ __forceinline__ void class_dots(const int* __restrict__ kw, const int
     for (int c = 0; c < kMaxClasses; ++c) {
         int acc = 0;
         if (c < nc) {
-            const int* w = wl + c * (D / 2) + col0;
+            // 16-byte LDS reads (broadcast: every thread reads the same class row)
+            const int4* w = reinterpret_cast<const int4*>(wl + c * (D / 2) + col0);
 #pragma unroll
-            for (int i = 0; i < D / 4; ++i) acc = dot4_i8(kw[i], w[i], acc);
+            for (int i = 0; i < D / 16; ++i) {
+                const int4 v = w[i];
+                acc = dot4_i8(kw[4 * i + 0], v.x, acc);
+                acc = dot4_i8(kw[4 * i + 1], v.y, acc);
+                acc = dot4_i8(kw[4 * i + 2], v.z, acc);
+                acc = dot4_i8(kw[4 * i + 3], v.w, acc);
+            }
         }
         u[c] = acc;
     }
@@ -50,7 +57,7 @@ __global__ __launch_bounds__(kChunk) void k_predict_chunks(const int8_t* __restr
                                                            const int8_t* __restrict__ W,
                                                            int32_t* __restrict__ tot, int T, int nc)
 {
-    __shared__ int wl[kMaxClasses * D / 2];
+    __shared__ __align__(16) int wl[kMaxClasses * D / 2];
     __shared__ int part[kChunk / 32][kMaxClasses + 1];
     __shared__ int us[kChunk][kMaxClasses + 1];
     const int nch = (int)chunks_per_pair(T);
@@ -94,10 +101,11 @@ __global__ __launch_bounds__(kChunk) void k_predict_final(const int8_t* __restri
                                                           int32_t* __restrict__ budget, int T,
                                                           int nc, int kpc, int cap)
 {
-    __shared__ int wl[kMaxClasses * D / 2];
+    __shared__ __align__(16) int wl[kMaxClasses * D / 2];
     __shared__ int us[kChunk][kMaxClasses + 1];
     __shared__ int off[kChunk / 32][kMaxClasses + 1];
     __shared__ int segoff[kChunk / 32][kMaxClasses + 1];
+    __shared__ int base[kChunk / 32][kMaxClasses + 1];
     const int nch = (int)chunks_per_pair(T);
     const int pair = blockIdx.x / nch, chunk = blockIdx.x % nch;
     stage_weights<D>(W, nc, wl);
@@ -135,6 +143,15 @@ __global__ __launch_bounds__(kChunk) void k_predict_final(const int8_t* __restri
         segoff[seg][c] = acc;
     }
     __syncthreads();
+    {   // per (segment, class): everything before the segment (earlier chunks
+        // and earlier segments of this chunk)
+        const int c = threadIdx.x % kMaxClasses, seg = threadIdx.x / kMaxClasses;
+        int acc = 0;
+        for (int g = 0; g < kChunk / kMaxClasses; ++g) acc += off[g][c];
+        for (int s2 = 0; s2 < seg; ++s2) acc += segoff[s2][c];
+        base[seg][c] = acc;
+    }
+    __syncthreads();
     if (!live) return;
     const int seg = threadIdx.x / 32;
     int qw[D / 4];
@@ -143,11 +160,16 @@ __global__ __launch_bounds__(kChunk) void k_predict_final(const int8_t* __restri
     for (int i = 0; i < D / 4; ++i) qw[i] = qr[i];
     int best = 0, best_z = 0;
     for (int c = 0; c < nc; ++c) {
-        int z = us[threadIdx.x][c];
-        for (int s2 = 0; s2 < seg; ++s2) z += segoff[s2][c];
-        for (int g = 0; g < kChunk / kMaxClasses; ++g) z += off[g][c];
-        const int* w = wl + c * (D / 2);
-        for (int i = 0; i < D / 4; ++i) z = dot4_i8(qw[i], w[i], z);
+        int z = us[threadIdx.x][c] + base[seg][c];
+        const int4* w = reinterpret_cast<const int4*>(wl + c * (D / 2));
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) {
+            const int4 v = w[i];
+            z = dot4_i8(qw[4 * i + 0], v.x, z);
+            z = dot4_i8(qw[4 * i + 1], v.y, z);
+            z = dot4_i8(qw[4 * i + 2], v.z, z);
+            z = dot4_i8(qw[4 * i + 3], v.w, z);
+        }
         if (c == 0 || z > best_z) {
             best = c;
             best_z = z;
