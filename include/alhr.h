@@ -218,8 +218,8 @@ alhr_status alhr_decode_step(const alhr_config *cfg, int32_t pos,
  * optimised dense kernel the openai-hub article asks comparisons to use:
  * O[t] = sum_{j <= t} softmax_j(scale * Q[t] . K[j]) V[j], fp32 output.
  * Uses batch, heads, T, d and scale of cfg (d = 32, 64, 128 or 256; other
- * built sizes return ALHR_ERR_UNSUPPORTED); the routing fields are checked
- * as for the other calls but not used. */
+ * built sizes, and batch * heads * T >= 2^31, return ALHR_ERR_UNSUPPORTED);
+ * the routing fields are checked as for the other calls but not used. */
 alhr_status alhr_dense_attend(const alhr_config *cfg, const int8_t *Q,
                               const int8_t *K, const float *V, float *O,
                               void *stream);

@@ -308,6 +308,8 @@ alhr_status alhr_dense_attend(const alhr_config* cfg, const int8_t* Q, const int
     if (cfg->d < 32)
         return fail(ALHR_ERR_UNSUPPORTED, "%s: d = %d is not built for the dense kernel (32, 64, "
                                           "128, 256)", fn, cfg->d);
+    if ((int64_t)s.P * s.T >= ((int64_t)1 << 31))   // one launch of 2 * P * T work-items
+        return fail(ALHR_ERR_UNSUPPORTED, "%s: batch * heads * T must stay below 2^31", fn);
     ALHR_NEED_PTR(Q);
     ALHR_NEED_PTR(K);
     ALHR_NEED_PTR(V);

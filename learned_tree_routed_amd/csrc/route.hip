@@ -444,12 +444,13 @@ __global__ __launch_bounds__(kThreads) void k_route(
     const int32_t* __restrict__ nodes, const int32_t* __restrict__ budget, int fixed_budget,
     int32_t* __restrict__ idx, int32_t* __restrict__ count, float* __restrict__ O,
     int32_t* __restrict__ stats, int P, int T, int L, int l16, int window, int max_budget,
-    float scale)
+    float scale, uint64_t q0, uint64_t nq)
 {
     __shared__ WaveLds smem[kWavesPerBlock];
     const int wid = uniform((int)(threadIdx.x / kWave));
-    const uint64_t gw = (uint64_t)xcd_logical_block() * kWavesPerBlock + wid;
-    if (gw >= (uint64_t)P * T) return;
+    const uint64_t lw = (uint64_t)xcd_logical_block() * kWavesPerBlock + wid;
+    if (lw >= nq) return;
+    const uint64_t gw = q0 + lw;   // query index over all P * T (launches cover ranges)
     const int pair = uniform((int)(gw / (uint64_t)T));
     const int t = uniform(T - 1 - (int)(gw % (uint64_t)T));
     const size_t qrow = (size_t)pair * T + t;
@@ -483,13 +484,15 @@ __global__ __launch_bounds__(kThreads) void k_attend(const int8_t* __restrict__ 
                                                      const int32_t* __restrict__ idx,
                                                      const int32_t* __restrict__ count,
                                                      float* __restrict__ O, int P, int T,
-                                                     int max_budget, float scale)
+                                                     int max_budget, float scale, uint64_t q0,
+                                                     uint64_t nq)
 {
     constexpr int LPR = D / 16, RPG = kWave / LPR;
     __shared__ WaveLds smem[kWavesPerBlock];
     const int wid = threadIdx.x / kWave;
-    const uint64_t gw = (uint64_t)xcd_logical_block() * kWavesPerBlock + wid;
-    if (gw >= (uint64_t)P * T) return;
+    const uint64_t lw = (uint64_t)xcd_logical_block() * kWavesPerBlock + wid;
+    if (lw >= nq) return;
+    const uint64_t gw = q0 + lw;   // query index over all P * T (launches cover ranges)
     const int pair = (int)(gw / (uint64_t)T);
     const int t = (int)(gw % (uint64_t)T);
     const size_t qrow = (size_t)pair * T + t;
@@ -731,6 +734,10 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_num_sgp
     attend_block<D>(bs, C, T, scale, V + (size_t)pair * T * D, O + (size_t)pair * D);
 }
 
+// One wave per query, and a dispatch's work-item count is 32-bit: launches
+// cover at most kQueriesPerLaunch queries each (2^30 work-items).
+constexpr uint64_t kQueriesPerLaunch = (uint64_t)1 << 24;
+
 unsigned grid_for_waves(uint64_t waves)
 {
     uint64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -743,20 +750,26 @@ hipError_t route_d(const Shape& s, const int8_t* Q, const int8_t* K, const float
                    const int32_t* nodes, const int32_t* budget, int fixed_budget, int32_t* idx,
                    int32_t* count, float* O, int32_t* stats, hipStream_t st)
 {
-    const dim3 grid(grid_for_waves((uint64_t)s.P * s.T));
-    if (stats)
-        hipLaunchKernelGGL((k_route<D, MUL24, false, true>), grid, dim3(kThreads), 0, st, Q, K, V,
-                           nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T, s.L,
-                           s.l16, s.window, s.max_budget, s.scale);
-    else if (O)
-        hipLaunchKernelGGL((k_route<D, MUL24, true, false>), grid, dim3(kThreads), 0, st, Q, K, V,
-                           nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T, s.L,
-                           s.l16, s.window, s.max_budget, s.scale);
-    else
-        hipLaunchKernelGGL((k_route<D, MUL24, false, false>), grid, dim3(kThreads), 0, st, Q, K,
-                           V, nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T, s.L,
-                           s.l16, s.window, s.max_budget, s.scale);
-    return hipGetLastError();
+    const uint64_t total = (uint64_t)s.P * s.T;
+    for (uint64_t q0 = 0; q0 < total; q0 += kQueriesPerLaunch) {
+        const uint64_t nq = total - q0 < kQueriesPerLaunch ? total - q0 : kQueriesPerLaunch;
+        const dim3 grid(grid_for_waves(nq));
+        if (stats)
+            hipLaunchKernelGGL((k_route<D, MUL24, false, true>), grid, dim3(kThreads), 0, st, Q, K,
+                               V, nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T,
+                               s.L, s.l16, s.window, s.max_budget, s.scale, q0, nq);
+        else if (O)
+            hipLaunchKernelGGL((k_route<D, MUL24, true, false>), grid, dim3(kThreads), 0, st, Q, K,
+                               V, nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T,
+                               s.L, s.l16, s.window, s.max_budget, s.scale, q0, nq);
+        else
+            hipLaunchKernelGGL((k_route<D, MUL24, false, false>), grid, dim3(kThreads), 0, st, Q,
+                               K, V, nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T,
+                               s.L, s.l16, s.window, s.max_budget, s.scale, q0, nq);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int D>
@@ -807,20 +820,26 @@ hipError_t launch_route(const Shape& s, const int8_t* Q, const int8_t* K, const 
 hipError_t launch_attend(const Shape& s, const int8_t* Q, const int8_t* K, const float* V,
                          const int32_t* idx, const int32_t* count, float* O, hipStream_t st)
 {
-    const dim3 grid(grid_for_waves((uint64_t)s.P * s.T));
-#define ALHR_ATTEND(DD)                                                                          \
-    hipLaunchKernelGGL((k_attend<DD>), grid, dim3(kThreads), 0, st, Q, K, V, idx, count, O, s.P, \
-                       s.T, s.max_budget, s.scale)
-    switch (s.d) {
-        case 16: ALHR_ATTEND(16); break;
-        case 32: ALHR_ATTEND(32); break;
-        case 64: ALHR_ATTEND(64); break;
-        case 128: ALHR_ATTEND(128); break;
-        case 256: ALHR_ATTEND(256); break;
-        default: return hipErrorInvalidValue;
-    }
+    const uint64_t total = (uint64_t)s.P * s.T;
+    for (uint64_t q0 = 0; q0 < total; q0 += kQueriesPerLaunch) {
+        const uint64_t nq = total - q0 < kQueriesPerLaunch ? total - q0 : kQueriesPerLaunch;
+        const dim3 grid(grid_for_waves(nq));
+#define ALHR_ATTEND(DD)                                                                           \
+    hipLaunchKernelGGL((k_attend<DD>), grid, dim3(kThreads), 0, st, Q, K, V, idx, count, O, s.P,  \
+                       s.T, s.max_budget, s.scale, q0, nq)
+        switch (s.d) {
+            case 16: ALHR_ATTEND(16); break;
+            case 32: ALHR_ATTEND(32); break;
+            case 64: ALHR_ATTEND(64); break;
+            case 128: ALHR_ATTEND(128); break;
+            case 256: ALHR_ATTEND(256); break;
+            default: return hipErrorInvalidValue;
+        }
 #undef ALHR_ATTEND
-    return hipGetLastError();
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_decode(const Shape& s, int pos, const int8_t* q_new, const int8_t* K,

@@ -249,3 +249,10 @@ def test_split_binding_checks_shapes_before_the_library():
     with pytest.raises(TypeError):
         alhr.alhr_split_qk(s, torch.zeros((1, 16, 32), dtype=torch.float32),
                            torch.zeros((64, 32), dtype=torch.int8))
+
+
+@pytestmark_cpu
+def test_dense_rejects_more_queries_than_one_launch_holds():
+    c = alhr.Config(batch=65536, heads=1, T=1 << 15, d=32, kmax=1, qmax=1, wmax=1)
+    st, msg = status("alhr_dense_attend", C.byref(c.c()), P0, P0, P0, P0, NULL)
+    assert st == -4 and "2^31" in msg, msg

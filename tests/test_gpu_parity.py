@@ -366,3 +366,45 @@ def test_dense_equals_routing_with_full_budget(torch_dev):
     routed = alhr.alhr_forward(cfg, q, k, v, None, fixed_budget=64)
     torch.cuda.synchronize()
     assert (dense - routed["O"]).abs().max().item() <= 1e-5
+
+
+def test_launches_split_by_query_range(torch_dev):
+    """More queries than one launch covers (2^24, so that the work-item count
+    of a dispatch stays 32-bit): 5 x 205 pairs of T = 16384 (16.8 M queries,
+    d = 16, budget 8) run as two launches of the route and attention kernels.
+    Every count is exact, and sampled queries of the pairs on both sides of the
+    split equal the oracle."""
+    import learned_tree_routed_amd as alhr
+    from synth import device as sd
+    from synth.workloads import pair_keys, pair_query_rows, pair_value_rows
+    torch, dev = torch_dev
+    B, H, T, d = 5, 205, 16384, 16
+    assert B * H * T > 1 << 24
+    w = Workload("split_launch", 9, B, H, T, d, "clustered", fixed_budget=8, max_budget=8)
+    cfg = w.config()
+    K = sd.keys_(torch.empty((B, H, T, d), dtype=torch.int8, device=dev), w.seed)
+    Q = sd.queries_(torch.empty((B, H, T, d), dtype=torch.int8, device=dev), w.seed)
+    V = sd.values_(torch.empty((B, H, T, d), dtype=torch.float32, device=dev), w.seed)
+    say("alhr_forward B5 H205 T16384 d16 fixed 8 (two launches per kernel)")
+    out = alhr.alhr_forward(cfg, Q, K, V, None, fixed_budget=8)
+    torch.cuda.synchronize()
+    want = torch.clamp(torch.arange(T, device=dev, dtype=torch.int32) + 1, max=8)
+    assert torch.equal(out["count"], want.expand(B, H, T))
+    # query index q = pair * T + (T - 1 - t) in the route kernel: the split at
+    # 2^24 falls between pairs 1023 = (4, 203) and 1024 = (4, 204)
+    ts = np.array([0, 1, 7, 8, 100, 5000, 12345, T - 2, T - 1])
+    for pair in (1023, 1024):
+        b, h = divmod(pair, H)
+        Kp = pair_keys(w, b, h)
+        Qp = pair_query_rows(w, b, h, np.arange(T))
+        Vp = pair_value_rows(w, b, h, np.arange(T))
+        ref = oracle.pair_forward(Qp, Kp, Vp, W=None, fixed_budget=8, window=cfg.window,
+                                  keys_per_class=cfg.keys_per_class, max_budget=8,
+                                  scale=cfg.scale, ts=ts)
+        np.testing.assert_array_equal(out["idx"][b, h].cpu().numpy()[ts], ref["idx"])
+        err = np.abs(out["O"][b, h].cpu().numpy()[ts] - ref["O"]).max()
+        assert err <= ATOL, "pair %d: max |O - oracle| = %g" % (pair, err)
+    # the attention kernel on its own over the same sets, also split
+    O2 = alhr.alhr_sparse_attend(cfg, Q, K, V, out["idx"], out["count"])
+    torch.cuda.synchronize()
+    assert torch.equal(O2, out["O"])
