@@ -157,6 +157,27 @@ __device__ __forceinline__ const int32_t* tree_row16(const int32_t* pair_table, 
                                             b16 * 4 * D + (r - b16) * 2 * D);
 }
 
+// A global-memory base known to be the same in every lane: kept in scalar
+// registers, so loads through it take the scalar-base form (SGPR base +
+// 32-bit lane offset) and each lane computes only a 32-bit byte offset.
+typedef const char __attribute__((address_space(1))) gbyte;
+
+__device__ __forceinline__ gbyte* uniform_base(const void* p)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<gbyte*>(((uint64_t)hi << 32) | lo);
+}
+
+// 16 bytes at byte offset `off` (16-byte aligned) from a uniform base.
+typedef int gvec4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int4 load16(gbyte* base, uint32_t off)
+{
+    const gvec4 v = *reinterpret_cast<const gvec4 __attribute__((address_space(1)))*>(base + off);
+    return make_int4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ int dot4_i8(int a, int b, int acc)
 {
     return __builtin_amdgcn_sdot4(a, b, acc, false);

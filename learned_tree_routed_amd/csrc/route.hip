@@ -114,18 +114,23 @@ __device__ __forceinline__ int score_node(const int32_t* __restrict__ nodes_pair
                                           const QueryRegs<D>& q)
 {
     constexpr int LPR = D / 16;
+    // per-pair tables are under 2^30 bytes: 32-bit byte offsets from a
+    // wave-uniform base (the scalar-base load form)
+    gbyte* nbase = uniform_base(nodes_pair);
+    gbyte* kbase = uniform_base(keys_pair);
+    const uint32_t b16 = (uint32_t)T >> l16;
     int acc = 0;
     if (active) {
+        const uint32_t r = ((uint32_t)T >> level) + ((uint32_t)start >> level);   // heap row
         if (level > l16) {
             // int32 row (block-interleaved, see wide_slot): block j = 2k + h
             // holds at slot s the columns 8c + 4h .. 8c + 4h + 3 of chunk
             // c = k * LPR + s, i.e. the query pairs qh[2j], qh[2j + 1].  The
             // pairs are unpacked here (these are the few top levels).
-            const int4* row = reinterpret_cast<const int4*>(
-                tree_row32<D>(nodes_pair, (size_t)((T >> level) + (start >> level))));
+            const uint32_t row = r * (uint32_t)(4 * D);
             int4 v[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = row[j * LPR + s];
+            for (int j = 0; j < 4; ++j) v[j] = load16(nbase, row + 16u * (uint32_t)(j * LPR + s));
             // an opaque copy keeps the unpacking here instead of letting it
             // be hoisted out of the descent loop into 16 live registers
             int qh[8];
@@ -142,12 +147,11 @@ __device__ __forceinline__ int score_node(const int32_t* __restrict__ nodes_pair
                 acc += imul<MUL24>(hi16(qh[2 * j + 1]), v[j].w);
             }
         } else if (level > 0) {
-            // int16 row: chunk c is int4 c
-            const int4* row = reinterpret_cast<const int4*>(
-                tree_row16<D>(nodes_pair, T, l16, (size_t)((T >> level) + (start >> level))));
+            // int16 row (the layout of tree_row16): chunk c is 16-byte slot c
+            const uint32_t row = b16 * (uint32_t)(4 * D) + (r - b16) * (uint32_t)(2 * D);
             int4 v[2];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) v[k] = row[k * LPR + s];
+            for (int k = 0; k < 2; ++k) v[k] = load16(nbase, row + 16u * (uint32_t)(k * LPR + s));
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 acc = dot2_i16(q.qh[4 * k + 0], v[k].x, acc);
@@ -156,7 +160,7 @@ __device__ __forceinline__ int score_node(const int32_t* __restrict__ nodes_pair
                 acc = dot2_i16(q.qh[4 * k + 3], v[k].w, acc);
             }
         } else {
-            const int4 v = reinterpret_cast<const int4*>(keys_pair + (size_t)start * D)[s];
+            const int4 v = load16(kbase, (uint32_t)start * (uint32_t)D + 16u * (uint32_t)s);
             acc = dot4_i8(q.qp[0], v.x, acc);
             acc = dot4_i8(q.qp[1], v.y, acc);
             acc = dot4_i8(q.qp[2], v.z, acc);
@@ -412,12 +416,15 @@ __device__ void attend_selected(WaveLds& sm, int C, int T, float scale,
     const float z = wave_sum_f(e0 + e1);
     wave_sync();
     const int cv = lane % LPV, rv = lane / LPV;
+    gbyte* vbase = uniform_base(values_pair);   // a pair's values are under 2^30 bytes
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c = rv; c < C; c += RPV) {
         const int j = sm.pos[c];
         if ((unsigned)j >= (unsigned)T) continue;
         const float wt = sm.w[c];
-        const float4 v = reinterpret_cast<const float4*>(values_pair + (size_t)j * D)[cv];
+        const int4 vi = load16(vbase, (uint32_t)j * (uint32_t)(4 * D) + 16u * (uint32_t)cv);
+        const float4 v = make_float4(__int_as_float(vi.x), __int_as_float(vi.y),
+                                     __int_as_float(vi.z), __int_as_float(vi.w));
         acc.x += wt * v.x;
         acc.y += wt * v.y;
         acc.z += wt * v.z;
