@@ -210,3 +210,33 @@ def test_decode_full_cache_sampled_pairs(torch_dev):
                                                                    time.time() - t_replay))
     del Kd, Vd, nodes
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T,d,fixed", [(64, 32, 0), (128, 16, 5), (2, 16, 1)])
+def test_decode_from_empty_cache_every_step(torch_dev, T, d, fixed):
+    """Decoding from position 0 to T - 1: the first steps are served by the
+    window alone (r = 0), the covers are tiny, and the last step fills the
+    cache; every step, the tree and the prefix equal the oracle's replay."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    w = Workload("decode_empty", 8, 1, 2, T, d, "clustered", fixed_budget=fixed)
+    cfg = w.config()
+    Q, K, V, W = host_inputs(w)
+    say("decode from empty: B1 H2 T%d d%d fixed %d" % (T, d, fixed))
+    Kd = torch.zeros((1, 2, T, d), dtype=torch.int8, device=dev)
+    Vd = torch.zeros((1, 2, T, d), dtype=torch.float32, device=dev)
+    nodes = alhr.alhr_build_tree(cfg, Kd)
+    prefix = alhr.alhr_prefix_from_tree(cfg, 0, Kd, nodes)
+    Wd = None if W is None else torch.from_numpy(W).to(dev)
+    Kh, Vh, Qh = (torch.from_numpy(x).to(dev) for x in (K, V, Q))
+    pairs = [(0, 0), (0, 1)]
+    got = run_decode(torch, dev, w, cfg, Kd, Vd, nodes, prefix, Wd, 0, T, pairs,
+                     lambda p: Qh[:, :, p].contiguous(), lambda p: Kh[:, :, p].contiguous(),
+                     lambda p: Vh[:, :, p].contiguous())
+    l16 = alhr.alhr_tree_int16_levels(cfg)
+    for (b, h) in pairs:
+        ref, ref_nodes, ref_pre = decode_oracle_pair(w, b, h, 0, T, K[b, h], Q[b, h], W, cfg)
+        compare(got[(b, h)], ref)
+        np.testing.assert_array_equal(decode_tree(nodes[b, h].cpu().numpy(), l16)[1:],
+                                      ref_nodes[1:])
+        np.testing.assert_array_equal(prefix[b, h].cpu().numpy(), ref_pre)
