@@ -285,11 +285,12 @@ def bench_decode(args, torch, dev):
         alhr.alhr_prefix_from_tree(cfg, n0, K, nodes, prefix)
 
     def loop():
+        # one launch per token: append the key and value, then route and attend
         for s in range(S):
-            alhr.alhr_append(cfg, n0 + s, ks[s], vs[s], K, V, nodes, prefix)
-            alhr.alhr_decode_step(cfg, n0 + s, qs[s], K, V, nodes, prefix, Wd, 0, bud, idx, cnt, O)
+            alhr.alhr_append_decode(cfg, n0 + s, ks[s], vs[s], qs[s], K, V, nodes, prefix, Wd, 0,
+                                    bud, idx, cnt, O)
 
-    # eager loop once (also the warm-up), then the same 2 x 128 launches
+    # eager loop once (also the warm-up), then the same 128 launches
     # captured in a HIP graph; each timed replay starts from a reset cache
     reset()
     torch.cuda.synchronize()
@@ -327,7 +328,7 @@ def bench_decode(args, torch, dev):
         "data": "synthetic (device-generated clustered keys, seeded)",
         "config": {"workload": "decode", "sequences": B, "heads": H, "T": T, "d": d,
                    "prefilled": n0, "tokens_per_step": S, "queries_per_step": queries,
-                   "launch": "HIP graph of 128 x (append, decode step)"},
+                   "launch": "HIP graph of 128 fused append + decode step launches"},
         "diagnostics": {"mean_keys_last_step": float(cnt.float().mean().item()),
                         "event_ms_per_step": float(np.mean([t[1] for t in times])),
                         "eager_ms_per_step": eager_ms},

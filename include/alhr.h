@@ -213,6 +213,21 @@ alhr_status alhr_decode_step(const alhr_config *cfg, int32_t pos,
                              int32_t *idx, int32_t *count, float *O,
                              void *stream);
 
+/* Append and decode step in one launch: alhr_append(pos, k_new, v_new)
+ * followed by alhr_decode_step(pos, q_new), with the same arguments, layouts,
+ * results and error codes (prefix is required).  Each (batch, head) pair's
+ * workgroup appends its own key and value rows before it routes, so no
+ * pair waits for another; this saves the second launch of every token step
+ * (openai-hub article "ALHR把注意力变成树搜索", section "ALHR是什么": one new
+ * token per step). */
+alhr_status alhr_append_decode(const alhr_config *cfg, int32_t pos,
+                               const int8_t *k_new, const float *v_new,
+                               const int8_t *q_new, int8_t *K, float *V,
+                               int32_t *nodes, int32_t *prefix, const int8_t *W,
+                               int32_t fixed_budget, int32_t *budget,
+                               int32_t *idx, int32_t *count, float *O,
+                               void *stream);
+
 /* Dense causal softmax attention over every past key, the baseline the
  * README's result tables compare against (dense teacher rows) and the
  * optimised dense kernel the openai-hub article asks comparisons to use:

@@ -24,7 +24,7 @@ __all__ = [
     "alhr_route_stats", "alhr_sparse_attend", "alhr_route_attend", "alhr_forward",
     "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_dense_attend",
     "alhr_status_string", "alhr_last_error", "alhr_version", "alhr_tree_int16_levels",
-    "alhr_split_qk", "SplitConfig", "EXPORTED",
+    "alhr_split_qk", "alhr_append_decode", "SplitConfig", "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +36,7 @@ EXPORTED = (
     "alhr_route_stats", "alhr_sparse_attend", "alhr_route_attend", "alhr_forward",
     "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_dense_attend",
     "alhr_status_string", "alhr_last_error", "alhr_version", "alhr_tree_int16_levels",
-    "alhr_split_qk",
+    "alhr_split_qk", "alhr_append_decode",
 )
 
 STATUS = {0: "ALHR_OK", -1: "ALHR_ERR_ARG", -2: "ALHR_ERR_OVERFLOW", -3: "ALHR_ERR_DEVICE",
@@ -144,6 +144,7 @@ def load():
         "alhr_prefix_from_tree": ([cfgp, i32, P, P, P, P], C.c_int),
         "alhr_append": ([cfgp, i32, P, P, P, P, P, P, P], C.c_int),
         "alhr_decode_step": ([cfgp, i32, P, P, P, P, P, P, i32, P, P, P, P, P], C.c_int),
+        "alhr_append_decode": ([cfgp, i32, P, P, P, P, P, P, P, P, i32, P, P, P, P, P], C.c_int),
         "alhr_dense_attend": ([cfgp, P, P, P, P, P], C.c_int),
         "alhr_status_string": ([C.c_int], C.c_char_p),
         "alhr_last_error": ([], C.c_char_p),
@@ -392,6 +393,34 @@ def alhr_decode_step(cfg, pos, q_new, K, V, nodes, prefix, W=None, fixed_budget=
     _call("alhr_decode_step", C.byref(cfg.c()), int(pos), _ptr(q_new), _ptr(K), _ptr(V),
           _ptr(nodes), _ptr(prefix), _ptr(W), int(fixed_budget), _ptr(budget), _ptr(idx),
           _ptr(count), _ptr(O), _stream(stream))
+    return idx, count, O
+
+
+def alhr_append_decode(cfg, pos, k_new, v_new, q_new, K, V, nodes, prefix, W=None,
+                       fixed_budget=0, budget=None, idx=None, count=None, O=None, stream=None):
+    """alhr_append(pos, k_new, v_new) and alhr_decode_step(pos, q_new) in one launch."""
+    torch = _torch()
+    rows, _, _ = _shapes(cfg)
+    one = (cfg.batch, cfg.heads, cfg.d)
+    _check("q_new", q_new, torch.int8, one)
+    dev = q_new.device
+    _check("k_new", k_new, torch.int8, one, dev)
+    _check("v_new", v_new, torch.float32, one, dev)
+    _check("K", K, torch.int8, rows, dev)
+    _check("V", V, torch.float32, rows, dev)
+    _check("nodes", nodes, torch.int32, rows, dev)
+    _check("prefix", prefix, torch.int32, one, dev)
+    if W is not None:
+        _check("W", W, torch.int8, (cfg.n_classes, 2 * cfg.d), dev)
+    per_pair = (cfg.batch, cfg.heads)
+    if budget is not None:
+        _check("budget", budget, torch.int32, per_pair, dev)
+    idx = _out(idx, "idx", torch.int32, (cfg.batch, cfg.heads, cfg.max_budget), dev)
+    count = _out(count, "count", torch.int32, per_pair, dev)
+    O = _out(O, "O", torch.float32, one, dev)
+    _call("alhr_append_decode", C.byref(cfg.c()), int(pos), _ptr(k_new), _ptr(v_new),
+          _ptr(q_new), _ptr(K), _ptr(V), _ptr(nodes), _ptr(prefix), _ptr(W), int(fixed_budget),
+          _ptr(budget), _ptr(idx), _ptr(count), _ptr(O), _stream(stream))
     return idx, count, O
 
 

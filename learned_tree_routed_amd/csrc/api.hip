@@ -382,17 +382,22 @@ alhr_status alhr_append(const alhr_config* cfg, int32_t pos, const int8_t* k_new
                                                  as_stream(stream)));
 }
 
-alhr_status alhr_decode_step(const alhr_config* cfg, int32_t pos, const int8_t* q_new,
-                             const int8_t* K, const float* V, const int32_t* nodes,
-                             const int32_t* prefix, const int8_t* W, int32_t fixed_budget,
-                             int32_t* budget, int32_t* idx, int32_t* count, float* O,
-                             void* stream)
+static alhr_status decode_common(const char* fn, const alhr_config* cfg, int32_t pos,
+                                 const int8_t* q_new, const int8_t* k_new, const float* v_new,
+                                 const int8_t* K, const float* V, const int32_t* nodes,
+                                 const int32_t* prefix, const int8_t* W, int32_t fixed_budget,
+                                 int32_t* budget, int32_t* idx, int32_t* count, float* O,
+                                 bool append, void* stream)
 {
-    const char* fn = "alhr_decode_step";
     alhr::Shape s;
     if (alhr_status st = check_config(fn, cfg, &s)) return st;
     if (pos < 0 || pos >= cfg->T) return fail(ALHR_ERR_ARG, "%s: pos = %d outside [0, T)", fn, pos);
     ALHR_NEED_PTR(q_new);
+    if (append) {
+        ALHR_NEED_PTR(k_new);
+        ALHR_NEED_PTR(v_new);
+        ALHR_NEED_PTR(prefix);
+    }
     ALHR_NEED_PTR(K);
     ALHR_NEED_PTR(V);
     ALHR_NEED_PTR(nodes);
@@ -409,9 +414,33 @@ alhr_status alhr_decode_step(const alhr_config* cfg, int32_t pos, const int8_t* 
     if (budget && !aligned16(budget))
         return fail(ALHR_ERR_ARG, "%s: argument 'budget' is not 16-byte aligned", fn);
     (void)hipGetLastError();
-    return device_status(fn, alhr::launch_decode(s, pos, q_new, K, V, nodes, prefix, W,
-                                                 fixed_budget, budget, idx, count, O,
-                                                 as_stream(stream)));
+    // the decode-only path reads K, V, nodes and prefix and never writes them
+    return device_status(fn, alhr::launch_decode(s, pos, q_new, append ? k_new : nullptr,
+                                                 append ? v_new : nullptr,
+                                                 const_cast<int8_t*>(K), const_cast<float*>(V),
+                                                 const_cast<int32_t*>(nodes),
+                                                 const_cast<int32_t*>(prefix), W, fixed_budget,
+                                                 budget, idx, count, O, as_stream(stream)));
+}
+
+alhr_status alhr_decode_step(const alhr_config* cfg, int32_t pos, const int8_t* q_new,
+                             const int8_t* K, const float* V, const int32_t* nodes,
+                             const int32_t* prefix, const int8_t* W, int32_t fixed_budget,
+                             int32_t* budget, int32_t* idx, int32_t* count, float* O,
+                             void* stream)
+{
+    return decode_common("alhr_decode_step", cfg, pos, q_new, nullptr, nullptr, K, V, nodes,
+                         prefix, W, fixed_budget, budget, idx, count, O, false, stream);
+}
+
+alhr_status alhr_append_decode(const alhr_config* cfg, int32_t pos, const int8_t* k_new,
+                               const float* v_new, const int8_t* q_new, int8_t* K, float* V,
+                               int32_t* nodes, int32_t* prefix, const int8_t* W,
+                               int32_t fixed_budget, int32_t* budget, int32_t* idx,
+                               int32_t* count, float* O, void* stream)
+{
+    return decode_common("alhr_append_decode", cfg, pos, q_new, k_new, v_new, K, V, nodes,
+                         prefix, W, fixed_budget, budget, idx, count, O, true, stream);
 }
 
 }  // extern "C"

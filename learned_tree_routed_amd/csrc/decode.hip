@@ -2,11 +2,10 @@
 // section "ALHR是什么": one new token per step; tree of key sums from the
 // ALHR README's opening paragraph).
 //
-// Append at position pos: the key and value rows are stored, the key is added
-// to each of the L ancestor sums (node (l, pos >> l), l = 1..L) and to the
-// running causal key sum.  One thread owns 4 columns of one pair, so the L
-// read-modify-writes of a pair are independent 16-byte accesses issued
-// back to back, and no two threads touch the same word.
+// Append at position pos (append.h): the key and value rows are stored, the
+// key is added to each of the L ancestor sums and to the running causal key
+// sum, one thread per 4 columns of a pair.
+#include "append.h"
 #include "device.h"
 #include "kernels.h"
 
@@ -14,11 +13,8 @@ namespace alhr {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxLevels = 20;   // T <= 2^20
-
-__device__ __forceinline__ int pack16(int lo, int hi) { return (lo & 0xFFFF) | (hi << 16); }
-__device__ __forceinline__ int lo16(int w) { return (int)(short)(w & 0xFFFF); }
-__device__ __forceinline__ int hi16(int w) { return w >> 16; }
+using appendk::hi16;
+using appendk::lo16;
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_append(const int8_t* __restrict__ k_new,
@@ -32,57 +28,8 @@ __global__ __launch_bounds__(kThreads) void k_append(const int8_t* __restrict__ 
     constexpr int C4 = D / 4;
     const int gid = blockIdx.x * kThreads + threadIdx.x;
     if (gid >= P * C4) return;
-    const int pair = gid / C4, g = gid % C4;
-    const int kw = reinterpret_cast<const int*>(k_new)[(size_t)pair * C4 + g];
-    const int4 kv = make_int4(sbyte(kw, 0), sbyte(kw, 1), sbyte(kw, 2), sbyte(kw, 3));
-    // key bytes of the even and the odd thread of this thread's pair g, g ^ 1
-    // (C4 is even, so both belong to the same (batch, head) pair)
-    const int kw_partner = __shfl_xor(kw, 1);
-    const int kw_even = (g & 1) ? kw_partner : kw, kw_odd = (g & 1) ? kw : kw_partner;
-    const size_t row = (size_t)pair * T + pos;
-    reinterpret_cast<int*>(K)[row * C4 + g] = kw;
-    reinterpret_cast<float4*>(V)[row * C4 + g] =
-        reinterpret_cast<const float4*>(v_new)[(size_t)pair * C4 + g];
-    // All L ancestor cells (and the running sum) are loaded before anything
-    // is stored, so the loads are in flight together instead of one
-    // dependent round trip per level.  Levels 1..l16 hold int16 rows, higher
-    // levels int32.  No load or store sits in a branch (a branch around a
-    // memory access makes the next one wait for it): every level is one
-    // 16-byte load and one 16-byte store at a selected address.  At an int16
-    // level, threads g and g ^ 1 share one 16-byte chunk (8 columns) and
-    // both write the same updated chunk.  The level loop runs to kMaxLevels
-    // with the level clamped to L, so it has no branch either: the extra
-    // iterations re-read and re-write the root with the same value.
-    int32_t* tree = nodes + (size_t)pair * T * D;
-    int4* pre = reinterpret_cast<int4*>(prefix) + (size_t)pair * C4 + g;
-    int4* cell_at[kMaxLevels];
-    int4 cells[kMaxLevels];
-#pragma unroll
-    for (int i = 1; i <= kMaxLevels; ++i) {
-        const int l = i < L ? i : L;
-        const size_t r = (size_t)((T >> l) + (pos >> l));
-        cell_at[i - 1] = l <= l16
-            ? reinterpret_cast<int4*>(const_cast<int32_t*>(tree_row16<D>(tree, T, l16, r))) +
-                  (g >> 1)
-            : reinterpret_cast<int4*>(tree + r * D) + wide_slot<D>(g);
-        cells[i - 1] = *cell_at[i - 1];
-    }
-    const int4 p = *pre;
-#pragma unroll
-    for (int i = 1; i <= kMaxLevels; ++i) {
-        const int l = i < L ? i : L;
-        const int4 c = cells[i - 1];
-        const int4 wide = make_int4(c.x + kv.x, c.y + kv.y, c.z + kv.z, c.w + kv.w);
-        const int4 narrow = make_int4(
-            pack16(lo16(c.x) + sbyte(kw_even, 0), hi16(c.x) + sbyte(kw_even, 1)),
-            pack16(lo16(c.y) + sbyte(kw_even, 2), hi16(c.y) + sbyte(kw_even, 3)),
-            pack16(lo16(c.z) + sbyte(kw_odd, 0), hi16(c.z) + sbyte(kw_odd, 1)),
-            pack16(lo16(c.w) + sbyte(kw_odd, 2), hi16(c.w) + sbyte(kw_odd, 3)));
-        const bool nar = l <= l16;   // per-component select, no int4 temporary
-        *cell_at[i - 1] = make_int4(nar ? narrow.x : wide.x, nar ? narrow.y : wide.y,
-                                    nar ? narrow.z : wide.z, nar ? narrow.w : wide.w);
-    }
-    *pre = make_int4(p.x + kv.x, p.y + kv.y, p.z + kv.z, p.w + kv.w);
+    appendk::append_columns<D>(gid / C4, gid % C4, k_new, v_new, K, V, nodes, prefix, T, L, l16,
+                               pos);
 }
 
 // prefix[pair] = sum of the maximal complete subtrees covering [0, n).

@@ -43,10 +43,13 @@ hipError_t launch_prefix_from_tree(const Shape& s, int n, const int8_t* K, const
 hipError_t launch_append(const Shape& s, int pos, const int8_t* k_new, const float* v_new,
                          int8_t* K, float* V, int32_t* nodes, int32_t* prefix, hipStream_t st);
 
-hipError_t launch_decode(const Shape& s, int pos, const int8_t* q_new, const int8_t* K,
-                         const float* V, const int32_t* nodes, const int32_t* prefix,
-                         const int8_t* W, int fixed_budget, int32_t* budget, int32_t* idx,
-                         int32_t* count, float* O, hipStream_t st);
+// k_new == nullptr: decode step only (the pair's rows are already appended);
+// otherwise append k_new / v_new at pos first, in the same launch.  The
+// decode-only path reads K, V, nodes and prefix without writing them.
+hipError_t launch_decode(const Shape& s, int pos, const int8_t* q_new, const int8_t* k_new,
+                         const float* v_new, int8_t* K, float* V, int32_t* nodes,
+                         int32_t* prefix, const int8_t* W, int fixed_budget, int32_t* budget,
+                         int32_t* idx, int32_t* count, float* O, hipStream_t st);
 
 hipError_t launch_dense(const Shape& s, const int8_t* Q, const int8_t* K, const float* V, float* O,
                         hipStream_t st);

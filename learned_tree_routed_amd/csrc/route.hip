@@ -25,6 +25,7 @@
 //    block; the final picks are sorted by counting ranks.
 //  * attention reuses the leaf scores as logits: fp32 softmax, then a gather
 //    of the C value rows with d/4 lanes per row (16 B each).
+#include "append.h"
 #include "device.h"
 #include "kernels.h"
 
@@ -708,10 +709,18 @@ __device__ void attend_block(BlockShared& bs, int C, int T, float scale,
     }
 }
 
-template <int D, bool MUL24>
+// APPEND: first store the new key and value rows at pos and add the key to
+// the pair's ancestor sums and running sum (append.h, spread over the
+// workgroup's threads),
+// then route and attend; the barrier between the two phases makes the
+// workgroup's global writes visible to its own reads (one CU, workgroup-scope
+// release and acquire).  Only the pair's own rows are touched, so workgroups
+// stay independent.
+template <int D, bool MUL24, bool APPEND>
 __global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_num_sgpr(80))) void k_decode(
-    const int8_t* __restrict__ q_new, const int8_t* __restrict__ K, const float* __restrict__ V,
-    const int32_t* __restrict__ nodes, const int32_t* __restrict__ prefix,
+    const int8_t* __restrict__ q_new, const int8_t* __restrict__ k_new,
+    const float* __restrict__ v_new, int8_t* __restrict__ K, float* __restrict__ V,
+    int32_t* __restrict__ nodes, int32_t* __restrict__ prefix,
     const int8_t* __restrict__ W, int fixed_budget, int32_t* __restrict__ budget_out,
     int32_t* __restrict__ idx, int32_t* __restrict__ count, float* __restrict__ O, int P, int T,
     int L, int l16, int pos, int window, int nc, int kpc, int max_budget, float scale)
@@ -719,6 +728,11 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_num_sgp
     __shared__ BlockShared bs;
     const uint32_t pair = xcd_logical_block();
     if (pair >= (uint32_t)P) return;   // uniform over the workgroup
+    if constexpr (APPEND) {
+        appendk::append_columns_spread<D, kDecodeWaves * kWave>((int)pair, k_new, v_new, K, V,
+                                                                nodes, prefix, T, L, l16, pos);
+        __syncthreads();
+    }
     const int lane = lane_id(), wv = threadIdx.x / kWave;
     const int s = lane % (D / 16);
     const int8_t* qp = q_new + (size_t)pair * D;
@@ -791,20 +805,26 @@ hipError_t route_dispatch(const Shape& s, const int8_t* Q, const int8_t* K, cons
 }
 
 template <int D>
-hipError_t decode_d(const Shape& s, int pos, const int8_t* q_new, const int8_t* K,
-                    const float* V, const int32_t* nodes, const int32_t* prefix, const int8_t* W,
-                    int fixed_budget, int32_t* budget, int32_t* idx, int32_t* count, float* O,
-                    hipStream_t st)
+hipError_t decode_d(const Shape& s, int pos, const int8_t* q_new, const int8_t* k_new,
+                    const float* v_new, int8_t* K, float* V, int32_t* nodes, int32_t* prefix,
+                    const int8_t* W, int fixed_budget, int32_t* budget, int32_t* idx,
+                    int32_t* count, float* O, hipStream_t st)
 {
     const dim3 grid((unsigned)((s.P + kXcds - 1) / kXcds * kXcds));
-    if (s.mul24)
-        hipLaunchKernelGGL((k_decode<D, true>), grid, dim3(kDecodeWaves * kWave), 0, st, q_new, K, V, nodes,
-                           prefix, W, fixed_budget, budget, idx, count, O, s.P, s.T, s.L, s.l16,
-                           pos, s.window, s.n_classes, s.keys_per_class, s.max_budget, s.scale);
-    else
-        hipLaunchKernelGGL((k_decode<D, false>), grid, dim3(kDecodeWaves * kWave), 0, st, q_new, K, V, nodes,
-                           prefix, W, fixed_budget, budget, idx, count, O, s.P, s.T, s.L, s.l16,
-                           pos, s.window, s.n_classes, s.keys_per_class, s.max_budget, s.scale);
+#define ALHR_DECODE(MUL, APP)                                                                     \
+    hipLaunchKernelGGL((k_decode<D, MUL, APP>), grid, dim3(kDecodeWaves * kWave), 0, st, q_new,    \
+                       k_new, v_new, K, V, nodes, prefix, W, fixed_budget, budget, idx, count, O, \
+                       s.P, s.T, s.L, s.l16, pos, s.window, s.n_classes, s.keys_per_class,      \
+                       s.max_budget, s.scale)
+    const bool append = k_new != nullptr;
+    if (s.mul24) {
+        if (append) ALHR_DECODE(true, true);
+        else ALHR_DECODE(true, false);
+    } else {
+        if (append) ALHR_DECODE(false, true);
+        else ALHR_DECODE(false, false);
+    }
+#undef ALHR_DECODE
     return hipGetLastError();
 }
 
@@ -849,19 +869,23 @@ hipError_t launch_attend(const Shape& s, const int8_t* Q, const int8_t* K, const
     return hipSuccess;
 }
 
-hipError_t launch_decode(const Shape& s, int pos, const int8_t* q_new, const int8_t* K,
-                         const float* V, const int32_t* nodes, const int32_t* prefix,
-                         const int8_t* W, int fixed_budget, int32_t* budget, int32_t* idx,
-                         int32_t* count, float* O, hipStream_t st)
+hipError_t launch_decode(const Shape& s, int pos, const int8_t* q_new, const int8_t* k_new,
+                         const float* v_new, int8_t* K, float* V, int32_t* nodes,
+                         int32_t* prefix, const int8_t* W, int fixed_budget, int32_t* budget,
+                         int32_t* idx, int32_t* count, float* O, hipStream_t st)
 {
+#define ALHR_DD(DD)                                                                               \
+    return decode_d<DD>(s, pos, q_new, k_new, v_new, K, V, nodes, prefix, W, fixed_budget, budget, \
+                        idx, count, O, st)
     switch (s.d) {
-        case 16: return decode_d<16>(s, pos, q_new, K, V, nodes, prefix, W, fixed_budget, budget, idx, count, O, st);
-        case 32: return decode_d<32>(s, pos, q_new, K, V, nodes, prefix, W, fixed_budget, budget, idx, count, O, st);
-        case 64: return decode_d<64>(s, pos, q_new, K, V, nodes, prefix, W, fixed_budget, budget, idx, count, O, st);
-        case 128: return decode_d<128>(s, pos, q_new, K, V, nodes, prefix, W, fixed_budget, budget, idx, count, O, st);
-        case 256: return decode_d<256>(s, pos, q_new, K, V, nodes, prefix, W, fixed_budget, budget, idx, count, O, st);
+        case 16: ALHR_DD(16);
+        case 32: ALHR_DD(32);
+        case 64: ALHR_DD(64);
+        case 128: ALHR_DD(128);
+        case 256: ALHR_DD(256);
         default: return hipErrorInvalidValue;
     }
+#undef ALHR_DD
 }
 
 }  // namespace alhr

@@ -167,6 +167,17 @@ def test_decode_and_append_argument_checks():
     assert lib.alhr_decode_step(cc, 5, P0, P0, P0, P0, P0, NULL, 0, NULL, P0, P0, P0, NULL) == -1
     # W given, prefix missing
     assert lib.alhr_decode_step(cc, 5, P0, P0, P0, P0, NULL, P0, 0, NULL, P0, P0, P0, NULL) == -1
+    # fused append + decode: the union of both entry points' checks
+    ad = lib.alhr_append_decode
+    assert ad(cc, 1024, P0, P0, P0, P0, P0, P0, P0, NULL, 16, NULL, P0, P0, P0, NULL) == -1
+    assert ad(cc, 5, NULL, P0, P0, P0, P0, P0, P0, NULL, 16, NULL, P0, P0, P0, NULL) == -1
+    assert ad(cc, 5, P0, NULL, P0, P0, P0, P0, P0, NULL, 16, NULL, P0, P0, P0, NULL) == -1
+    # prefix is required even with a fixed budget
+    assert ad(cc, 5, P0, P0, P0, P0, P0, P0, NULL, NULL, 16, NULL, P0, P0, P0, NULL) == -1
+    assert ad(cc, 5, P0, P0, P0, P0, P0, P0, P0, NULL, 0, NULL, P0, P0, P0, NULL) == -1
+    assert ad(cc, 5, P0, P0, P0, P0, P0, P0, P0, NULL, 97, NULL, P0, P0, P0, NULL) == -1
+    # a valid call reaches the device and fails there without a GPU
+    assert ad(cc, 5, P0, P0, P0, P0, P0, P0, P0, NULL, 16, NULL, P0, P0, P0, NULL) == -3
     assert lib.alhr_prefix_from_tree(cc, 1025, P0, P0, P0, NULL) == -1
     assert lib.alhr_sparse_attend(cc, P0, P0, NULL, P0, P0, P0, NULL) == -1
     assert lib.alhr_build_tree(None, P0, P0, NULL) == -1

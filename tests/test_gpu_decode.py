@@ -92,7 +92,9 @@ def decode_oracle_pair(w, b, h, n0, steps, K_pair, q_rows, W, cfg):
 
 
 def run_decode(torch, dev, w, cfg, K_dev, V_dev, nodes, prefix, W_dev, n0, steps, pairs,
-               q_src, k_src, v_src):
+               q_src, k_src, v_src, fused=False):
+    """fused: alhr_append_decode (one launch per step), else alhr_append then
+    alhr_decode_step."""
     import learned_tree_routed_amd as alhr
     got = {pr: [] for pr in pairs}
     bsel = torch.tensor([p[0] for p in pairs], device=dev)
@@ -100,10 +102,15 @@ def run_decode(torch, dev, w, cfg, K_dev, V_dev, nodes, prefix, W_dev, n0, steps
     for s in range(steps):
         p = n0 + s
         k_new, v_new, q_new = k_src(p), v_src(p), q_src(p)
-        alhr.alhr_append(cfg, p, k_new, v_new, K_dev, V_dev, nodes, prefix)
         bud = torch.empty((cfg.batch, cfg.heads), dtype=torch.int32, device=dev)
-        idx, cnt, O = alhr.alhr_decode_step(cfg, p, q_new, K_dev, V_dev, nodes, prefix, W_dev,
-                                            fixed_budget=w.fixed_budget, budget=bud)
+        if fused:
+            idx, cnt, O = alhr.alhr_append_decode(cfg, p, k_new, v_new, q_new, K_dev, V_dev, nodes,
+                                                  prefix, W_dev, fixed_budget=w.fixed_budget,
+                                                  budget=bud)
+        else:
+            alhr.alhr_append(cfg, p, k_new, v_new, K_dev, V_dev, nodes, prefix)
+            idx, cnt, O = alhr.alhr_decode_step(cfg, p, q_new, K_dev, V_dev, nodes, prefix, W_dev,
+                                                fixed_budget=w.fixed_budget, budget=bud)
         sb, si, sc, so = (bud[bsel, hsel].cpu().numpy(), idx[bsel, hsel].cpu().numpy(),
                           cnt[bsel, hsel].cpu().numpy(), O[bsel, hsel].cpu().numpy())
         for k, pr in enumerate(pairs):
@@ -122,8 +129,9 @@ def compare(got, ref):
         assert err <= ATOL, "step %d: max |O - oracle| = %g" % (s, err)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_launches", "fused"])
 @pytest.mark.parametrize("d,fixed", [(128, 0), (64, 0), (32, 20)])
-def test_decode_small_every_step(torch_dev, d, fixed):
+def test_decode_small_every_step(torch_dev, d, fixed, fused):
     import learned_tree_routed_amd as alhr
     torch, dev = torch_dev
     T, n0, steps = 4096, 4096 - 48, 48
@@ -142,7 +150,7 @@ def test_decode_small_every_step(torch_dev, d, fixed):
     pairs = [(b, h) for b in range(2) for h in range(3)]
     got = run_decode(torch, dev, w, cfg, Kd, Vd, nodes, prefix, Wd, n0, steps, pairs,
                      lambda p: Qh[:, :, p].contiguous(), lambda p: Kh[:, :, p].contiguous(),
-                     lambda p: Vh[:, :, p].contiguous())
+                     lambda p: Vh[:, :, p].contiguous(), fused=fused)
     l16 = alhr.alhr_tree_int16_levels(cfg)
     for (b, h) in pairs:
         ref, ref_nodes, ref_pre = decode_oracle_pair(w, b, h, n0, steps, K[b, h], Q[b, h, n0:], W, cfg)
@@ -164,9 +172,11 @@ def test_decode_small_every_step(torch_dev, d, fixed):
         np.testing.assert_array_equal(last[1], full["idx"][b, h, T - 1].cpu().numpy())
 
 
-def test_decode_full_cache_sampled_pairs(torch_dev):
+@pytest.mark.parametrize("fused", [False, True], ids=["two_launches", "fused"])
+def test_decode_full_cache_sampled_pairs(torch_dev, fused):
     """64 x 16 pairs, capacity 2^17, d = 128, 2^17 - 128 prefilled keys and
-    128 appended tokens: every step compared on 8 sampled pairs."""
+    128 appended tokens: every step compared on 8 sampled pairs.  The fused
+    case is the launch configuration the decode bench times."""
     import learned_tree_routed_amd as alhr
     from synth import device as sd
     torch, dev = torch_dev
@@ -191,7 +201,7 @@ def test_decode_full_cache_sampled_pairs(torch_dev):
     got = run_decode(torch, dev, w, cfg, Kd, Vd, nodes, prefix, Wd, n0, steps, pairs,
                      lambda p: sd.queries_(qbuf, w.seed, p, 1).view(B, H, d),
                      lambda p: sd.keys_(kbuf, w.seed, p, 1).view(B, H, d),
-                     lambda p: sd.values_(vbuf, w.seed, p, 1).view(B, H, d))
+                     lambda p: sd.values_(vbuf, w.seed, p, 1).view(B, H, d), fused=fused)
     say("decode full cache: device steps done, oracle replay of %d pairs" % len(pairs))
     import time
     t_replay = time.time()
@@ -212,8 +222,9 @@ def test_decode_full_cache_sampled_pairs(torch_dev):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("T,d,fixed", [(64, 32, 0), (128, 16, 5), (2, 16, 1)])
-def test_decode_from_empty_cache_every_step(torch_dev, T, d, fixed):
+@pytest.mark.parametrize("fused", [False, True], ids=["two_launches", "fused"])
+@pytest.mark.parametrize("T,d,fixed", [(64, 32, 0), (128, 16, 5), (2, 16, 1), (256, 256, 0)])
+def test_decode_from_empty_cache_every_step(torch_dev, T, d, fixed, fused):
     """Decoding from position 0 to T - 1: the first steps are served by the
     window alone (r = 0), the covers are tiny, and the last step fills the
     cache; every step, the tree and the prefix equal the oracle's replay."""
@@ -232,7 +243,7 @@ def test_decode_from_empty_cache_every_step(torch_dev, T, d, fixed):
     pairs = [(0, 0), (0, 1)]
     got = run_decode(torch, dev, w, cfg, Kd, Vd, nodes, prefix, Wd, 0, T, pairs,
                      lambda p: Qh[:, :, p].contiguous(), lambda p: Kh[:, :, p].contiguous(),
-                     lambda p: Vh[:, :, p].contiguous())
+                     lambda p: Vh[:, :, p].contiguous(), fused=fused)
     l16 = alhr.alhr_tree_int16_levels(cfg)
     for (b, h) in pairs:
         ref, ref_nodes, ref_pre = decode_oracle_pair(w, b, h, 0, T, K[b, h], Q[b, h], W, cfg)
