@@ -171,6 +171,61 @@ __device__ __forceinline__ int score_node(const int32_t* __restrict__ nodes_pair
     return group_sum<LPR>(acc);
 }
 
+// Left-child scoring inside the descent, from the child's heap row r =
+// (T + start) >> level (exact: start is a multiple of 2^level) instead of
+// (level, start).  The lane-dependent parts of the byte offsets are computed
+// once per query: o16 = 2d * (T >> l16) + 16 s (an int16 row r starts at
+// 2d * (r + (T >> l16)) in the packed layout), okey = 16 s - T d (key row
+// r - T starts at d * (r - T); the sum wraps modulo 2^32 to the exact
+// offset).  Inactive lanes contribute 0.
+template <int D, bool MUL24>
+__device__ __forceinline__ int score_row(gbyte* nbase, gbyte* nbase_hi, gbyte* kbase, uint32_t r,
+                                         int level, int l16, bool active, int s, uint32_t o16,
+                                         uint32_t okey, const QueryRegs<D>& q)
+{
+    constexpr int LPR = D / 16;
+    int acc = 0;
+    if (active) {
+        if (level > l16) {
+            const uint32_t row = r * (uint32_t)(4 * D);
+            int4 v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = load16(nbase, row + 16u * (uint32_t)(j * LPR + s));
+            int qh[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                qh[j] = q.qh[j];
+                asm volatile("" : "+v"(qh[j]));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc += imul<MUL24>(lo16(qh[2 * j]), v[j].x);
+                acc += imul<MUL24>(hi16(qh[2 * j]), v[j].y);
+                acc += imul<MUL24>(lo16(qh[2 * j + 1]), v[j].z);
+                acc += imul<MUL24>(hi16(qh[2 * j + 1]), v[j].w);
+            }
+        } else if (level > 0) {
+            const uint32_t off = r * (uint32_t)(2 * D) + o16;
+            const int4 v0 = load16(nbase, off), v1 = load16(nbase_hi, off);
+            acc = dot2_i16(q.qh[0], v0.x, acc);
+            acc = dot2_i16(q.qh[1], v0.y, acc);
+            acc = dot2_i16(q.qh[2], v0.z, acc);
+            acc = dot2_i16(q.qh[3], v0.w, acc);
+            acc = dot2_i16(q.qh[4], v1.x, acc);
+            acc = dot2_i16(q.qh[5], v1.y, acc);
+            acc = dot2_i16(q.qh[6], v1.z, acc);
+            acc = dot2_i16(q.qh[7], v1.w, acc);
+        } else {
+            const int4 v = load16(kbase, r * (uint32_t)D + okey);
+            acc = dot4_i8(q.qp[0], v.x, acc);
+            acc = dot4_i8(q.qp[1], v.y, acc);
+            acc = dot4_i8(q.qp[2], v.z, acc);
+            acc = dot4_i8(q.qp[3], v.w, acc);
+        }
+    }
+    return group_sum<LPR>(acc);
+}
+
 // A threshold x in [0, span] that selects the `need` largest values rel over
 // the wave (NS values per lane; zeros never count for x >= 1): bits are
 // decided from the most significant down, x | bit being kept when at least
@@ -349,28 +404,43 @@ __device__ int route_query(const int32_t* __restrict__ nodes_pair,
     int nb = select_best(sm.cand, L, r, sm.beam, inner);
     wave_sync();
 
+    // the descent's loop invariants (see score_row)
+    gbyte* nbase = uniform_base(nodes_pair);
+    gbyte* nbase_hi = nbase + 16 * LPR;   // second 16-byte chunk of an int16 row
+    gbyte* kbase = uniform_base(keys_pair);
+    const uint32_t o16 = (uint32_t)(2 * D) * ((uint32_t)T >> l16) + 16u * (uint32_t)s;
+    const uint32_t okey = 16u * (uint32_t)s - (uint32_t)T * (uint32_t)D;
+    const uint32_t tstart = (uint32_t)T + 0xFFFFFu;   // T + start = tstart - (lo >> 5)
     while (inner) {
         for (int base = 0; base < nb; base += RPG) {
+            // i < 128 = kMaxBudget (base < nb <= 127 is a multiple of RPG,
+            // which divides 128): entries past nb are read and their two
+            // candidate slots (< 2 * kMaxBudget) written, but never used
             const int i = base + g;
-            const uint64_t key = i < nb ? sm.beam[i] : 0ull;
-            const int lv = key_level(key), st = key_start(key);
+            const uint64_t key = sm.beam[i];
+            const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
+            const int lv = (int)(lo & 31u);
             const bool expand = i < nb && lv > 0;
             const int cl = lv - 1;
-            const int left = score_node<D, MUL24>(nodes_pair, keys_pair, T, l16, cl, st, expand, s, q);
+            const uint32_t row = (tstart - (lo >> 5)) >> ((uint32_t)cl & 31u);
+            const int left = score_row<D, MUL24>(nbase, nbase_hi, kbase, row, cl, l16, expand, s,
+                                                 o16, okey, q);
             if (STATS) {
                 cnt.tree_rows += wave_count(expand && s == 0 && cl > l16);
                 cnt.tree16_rows += wave_count(expand && s == 0 && cl > 0 && cl <= l16);
                 cnt.key_rows += wave_count(expand && s == 0 && cl == 0);
             }
-            if (i < nb && s == 0) {
-                if (expand) {
-                    sm.cand[2 * i] = make_key(left, st, cl);
-                    sm.cand[2 * i + 1] = make_key(key_score(key) - left, st + (1 << cl), cl);
-                } else {
-                    sm.cand[2 * i] = key;
-                    sm.cand[2 * i + 1] = 0ull;
-                }
-            }
+            // children from the parent key: the left child keeps the start
+            // and has level lv - 1 (low word - 1); the right child starts
+            // 2^cl later (low word - 1 - 32 * 2^cl) and scores parent - left
+            // (biased high word - left).  Every lane of the row group stores
+            // the same two keys.
+            const uint64_t c0 = expand ? ((uint64_t)((uint32_t)left ^ 0x80000000u) << 32) | (lo - 1u) : key;
+            const uint64_t c1 = expand
+                ? ((uint64_t)(hi - (uint32_t)left) << 32) | (lo - 1u - (32u << ((uint32_t)cl & 31u)))
+                : 0ull;
+            sm.cand[2 * i] = c0;
+            sm.cand[2 * i + 1] = c1;
         }
         wave_sync();
         nb = select_best(sm.cand, 2 * nb, r, sm.beam, inner);
@@ -419,17 +489,35 @@ __device__ void attend_selected(WaveLds& sm, int C, int T, float scale,
     const int cv = lane % LPV, rv = lane / LPV;
     gbyte* vbase = uniform_base(values_pair);   // a pair's values are under 2^30 bytes
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int c = rv; c < C; c += RPV) {
-        const int j = sm.pos[c];
-        if ((unsigned)j >= (unsigned)T) continue;
-        const float wt = sm.w[c];
-        const int4 vi = load16(vbase, (uint32_t)j * (uint32_t)(4 * D) + 16u * (uint32_t)cv);
-        const float4 v = make_float4(__int_as_float(vi.x), __int_as_float(vi.y),
-                                     __int_as_float(vi.z), __int_as_float(vi.w));
-        acc.x += wt * v.x;
-        acc.y += wt * v.y;
-        acc.z += wt * v.z;
-        acc.w += wt * v.w;
+    // kU rows per lane group in flight: their loads are issued before the
+    // first use.  A slot past C or holding a position outside [0, T) reads
+    // value row 0 and adds nothing (its row is replaced by zeros, so even a
+    // non-finite row 0 leaves the sum unchanged).
+    constexpr int kU = 4;
+    for (int c0 = 0; c0 < C; c0 += kU * RPV) {
+        int4 vi[kU];
+        float wt[kU];
+        bool ok[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int c = c0 + u * RPV + rv;
+            const int cc = c < kMaxBudget ? c : kMaxBudget - 1;
+            const int j = sm.pos[cc];
+            ok[u] = c < C && (unsigned)j < (unsigned)T;
+            wt[u] = sm.w[cc];
+            vi[u] = load16(vbase, (ok[u] ? (uint32_t)j : 0u) * (uint32_t)(4 * D) + 16u * (uint32_t)cv);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (!ok[u]) {
+                wt[u] = 0.0f;
+                vi[u] = make_int4(0, 0, 0, 0);
+            }
+            acc.x += wt[u] * __int_as_float(vi[u].x);
+            acc.y += wt[u] * __int_as_float(vi[u].y);
+            acc.z += wt[u] * __int_as_float(vi[u].z);
+            acc.w += wt[u] * __int_as_float(vi[u].w);
+        }
     }
 #pragma unroll
     for (int o = LPV; o < kWave; o <<= 1) {
