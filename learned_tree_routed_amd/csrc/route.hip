@@ -694,6 +694,13 @@ __device__ int route_query_block(const int32_t* __restrict__ nodes_pair,
         if (b < L && s == 0) sm.cand[L - 1 - b] = act ? make_key(sc, start, b) : 0ull;
     }
     __syncthreads();
+    // the descent's loop invariants (see score_row)
+    gbyte* nbase = uniform_base(nodes_pair);
+    gbyte* nbase_hi = nbase + 16 * LPR;
+    gbyte* kbase = uniform_base(keys_pair);
+    const uint32_t o16 = (uint32_t)(2 * D) * ((uint32_t)T >> l16) + 16u * (uint32_t)s;
+    const uint32_t okey = 16u * (uint32_t)s - (uint32_t)T * (uint32_t)D;
+    const uint32_t tstart = (uint32_t)T + 0xFFFFFu;
     int ncand = L;
     for (;;) {
         if (wv == 0) {
@@ -710,19 +717,22 @@ __device__ int route_query_block(const int32_t* __restrict__ nodes_pair,
         if (!uniform(bs.inner)) break;
         for (int base = 0; base < nb; base += RPB) {
             const int i = base + e0;
-            const uint64_t key = i < nb ? sm.beam[i] : 0ull;
-            const int lv = key_level(key), st = key_start(key);
-            const bool expand = i < nb && lv > 0;
+            const bool valid = i < nb;
+            const uint64_t key = sm.beam[valid ? i : 0];
+            const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
+            const int lv = (int)(lo & 31u);
+            const bool expand = valid && lv > 0;
             const int cl = lv - 1;
-            const int left = score_node<D, MUL24>(nodes_pair, keys_pair, T, l16, cl, st, expand, s, q);
-            if (i < nb && s == 0) {
-                if (expand) {
-                    sm.cand[2 * i] = make_key(left, st, cl);
-                    sm.cand[2 * i + 1] = make_key(key_score(key) - left, st + (1 << cl), cl);
-                } else {
-                    sm.cand[2 * i] = key;
-                    sm.cand[2 * i + 1] = 0ull;
-                }
+            const uint32_t row = (tstart - (lo >> 5)) >> ((uint32_t)cl & 31u);
+            const int left = score_row<D, MUL24>(nbase, nbase_hi, kbase, row, cl, l16, expand, s,
+                                                 o16, okey, q);
+            // children from the parent key (as in route_query); every lane of
+            // the row group stores the same two keys
+            if (valid) {
+                sm.cand[2 * i] = expand ? ((uint64_t)((uint32_t)left ^ 0x80000000u) << 32) | (lo - 1u) : key;
+                sm.cand[2 * i + 1] = expand
+                    ? ((uint64_t)(hi - (uint32_t)left) << 32) | (lo - 1u - (32u << ((uint32_t)cl & 31u)))
+                    : 0ull;
             }
         }
         ncand = 2 * nb;
@@ -762,16 +772,35 @@ __device__ void attend_block(BlockShared& bs, int C, int T, float scale,
     }
     __syncthreads();
     const int cv = lane % LPV, rv = lane / LPV;
+    gbyte* vbase = uniform_base(values_pair);   // a pair's values are under 2^30 bytes
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int c = wv * RPV + rv; c < C; c += RPB) {
-        const int j = sm.pos[c];
-        if ((unsigned)j >= (unsigned)T) continue;
-        const float wt = sm.w[c];
-        const float4 v = reinterpret_cast<const float4*>(values_pair + (size_t)j * D)[cv];
-        acc.x += wt * v.x;
-        acc.y += wt * v.y;
-        acc.z += wt * v.z;
-        acc.w += wt * v.w;
+    // as in attend_selected: kU rows in flight per lane group, slots past C
+    // or holding a position outside [0, T) add nothing
+    constexpr int kU = 4;
+    for (int c0 = wv * RPV + rv; c0 < C; c0 += kU * RPB) {
+        int4 vi[kU];
+        float wt[kU];
+        bool ok[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int c = c0 + u * RPB;
+            const int cc = c < kMaxBudget ? c : kMaxBudget - 1;
+            const int j = sm.pos[cc];
+            ok[u] = c < C && (unsigned)j < (unsigned)T;
+            wt[u] = sm.w[cc];
+            vi[u] = load16(vbase, (ok[u] ? (uint32_t)j : 0u) * (uint32_t)(4 * D) + 16u * (uint32_t)cv);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (!ok[u]) {
+                wt[u] = 0.0f;
+                vi[u] = make_int4(0, 0, 0, 0);
+            }
+            acc.x += wt[u] * __int_as_float(vi[u].x);
+            acc.y += wt[u] * __int_as_float(vi[u].y);
+            acc.z += wt[u] * __int_as_float(vi[u].z);
+            acc.w += wt[u] * __int_as_float(vi[u].w);
+        }
     }
 #pragma unroll
     for (int o = LPV; o < kWave; o <<= 1) {
