@@ -72,44 +72,49 @@ template <int G> __device__ __forceinline__ int group_sum(int v)
 }
 
 // Whole-wave reductions returning a wave-uniform value: butterfly within each
-// 16-lane row by DPP, then the four row results combined with readlane.
-template <typename Op> __device__ __forceinline__ int wave_reduce_i(int v, Op op)
+// 16-lane row by DPP (every lane then holds its row's result), then
+// row_bcast:15 folds rows 0 and 2 into rows 1 and 3 and row_bcast:31 folds
+// row 1 into rows 2 and 3, so lane 63 holds the result.  Rows left out by the
+// row mask keep `id` as the DPP operand (the identity of op).
+template <int CTRL, int ROWS> __device__ __forceinline__ int dpp_rows(int id, int v)
+{
+    return __builtin_amdgcn_update_dpp(id, v, CTRL, ROWS, 0xF, false);
+}
+template <typename Op> __device__ __forceinline__ int wave_reduce_i(int v, int id, Op op)
 {
     v = op(v, dpp<0xB1>(v));
     v = op(v, dpp<0x4E>(v));
     v = op(v, dpp<0x141>(v));
     v = op(v, dpp<0x140>(v));
-    const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-    const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-    return uniform(op(op(a, b), op(c, d)));
+    v = op(v, dpp_rows<0x142, 0xA>(id, v));
+    v = op(v, dpp_rows<0x143, 0xC>(id, v));
+    return __builtin_amdgcn_readlane(v, 63);
 }
-template <typename Op> __device__ __forceinline__ float wave_reduce_f(float v, Op op)
+template <typename Op> __device__ __forceinline__ float wave_reduce_f(float v, float id, Op op)
 {
     v = op(v, dppf<0xB1>(v));
     v = op(v, dppf<0x4E>(v));
     v = op(v, dppf<0x141>(v));
     v = op(v, dppf<0x140>(v));
-    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return op(op(a, b), op(c, d));
+    v = op(v, __int_as_float(dpp_rows<0x142, 0xA>(__float_as_int(id), __float_as_int(v))));
+    v = op(v, __int_as_float(dpp_rows<0x143, 0xC>(__float_as_int(id), __float_as_int(v))));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-    return (uint32_t)wave_reduce_i((int)v, [](int a, int b) { return (int)((uint32_t)a > (uint32_t)b ? a : b); });
+    return (uint32_t)wave_reduce_i((int)v, 0, [](int a, int b) { return (int)((uint32_t)a > (uint32_t)b ? a : b); });
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
 {
-    return (uint32_t)wave_reduce_i((int)v, [](int a, int b) { return (int)((uint32_t)a < (uint32_t)b ? a : b); });
+    return (uint32_t)wave_reduce_i((int)v, -1, [](int a, int b) { return (int)((uint32_t)a < (uint32_t)b ? a : b); });
 }
 __device__ __forceinline__ float wave_max_f(float v)
 {
-    return wave_reduce_f(v, [](float a, float b) { return a > b ? a : b; });
+    return wave_reduce_f(v, -INFINITY, [](float a, float b) { return a > b ? a : b; });
 }
 __device__ __forceinline__ float wave_sum_f(float v)
 {
-    return wave_reduce_f(v, [](float a, float b) { return a + b; });
+    return wave_reduce_f(v, 0.0f, [](float a, float b) { return a + b; });
 }
 
 // Generic shuffle reduction, for the rare wider types.
