@@ -233,21 +233,67 @@ __device__ __forceinline__ int score_row(gbyte* nbase, gbyte* nbase_hi, gbyte* k
 // reach x, since {rel >= x} is then the answer; otherwise it ends at the
 // largest x with at least `need` values >= x (ties at x are the caller's).
 // x = 0 is returned when no x >= 1 qualifies.  Wave-uniform.
+//
+// The loop is written out in scalar code: per bit one s_or, NS compares
+// (v_cmp into SGPR pairs), NS population counts, a compare-select and the two
+// exits, about half the scalar instructions the compiler makes of it.  All
+// lanes must be active (every caller runs with a full wave).
+#define ALHR_BS_HEAD "1:\n s_or_b32 %[c], %[x], %[bit]\n"
+#define ALHR_BS_CMP(J) "v_cmp_le_u32_e64 %[m" #J "], %[c], %[r" #J "]\n"
+#define ALHR_BS_CNT(J) "s_bcnt1_i32_b64 %[t" #J "], %[m" #J "]\n"
+#define ALHR_BS_TAIL(T)                                                                 \
+    "s_cmp_ge_i32 " T ", %[need]\n s_cselect_b32 %[x], %[c], %[x]\n"                    \
+    "s_cmp_eq_u32 " T ", %[need]\n s_cbranch_scc1 2f\n"                                 \
+    "s_lshr_b32 %[bit], %[bit], 1\n s_cbranch_scc1 1b\n 2:\n"
 template <int NS>
 __device__ __forceinline__ uint32_t bit_search(const uint32_t (&rel)[NS], uint32_t span, int need)
 {
+    static_assert(NS >= 1 && NS <= 4, "slots per lane");
     uint32_t x = 0u;
-    for (uint32_t bit = span ? 0x80000000u >> __builtin_clz(span) : 0u; bit; bit >>= 1) {
-        const uint32_t c = x | bit;
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < NS; ++j) cnt += wave_count(rel[j] >= c);
-        if (cnt >= need) x = c;
-        x = uniform(x);
-        if (cnt == need) break;
+    if (span == 0u) return x;
+    uint32_t bit = 0x80000000u >> __builtin_clz(span);
+    uint32_t c, t0, t1, t2, t3;
+    uint64_t m0, m1, m2, m3;
+    if constexpr (NS == 1) {
+        asm volatile(ALHR_BS_HEAD ALHR_BS_CMP(0) ALHR_BS_CNT(0) ALHR_BS_TAIL("%[t0]")
+                     : [x] "+s"(x), [bit] "+s"(bit), [c] "=&s"(c), [t0] "=&s"(t0), [m0] "=&s"(m0)
+                     : [r0] "v"(rel[0]), [need] "s"(need)
+                     : "scc");
+    } else if constexpr (NS == 2) {
+        asm volatile(ALHR_BS_HEAD ALHR_BS_CMP(0) ALHR_BS_CMP(1) ALHR_BS_CNT(0) ALHR_BS_CNT(1)
+                     "s_add_u32 %[t0], %[t0], %[t1]\n" ALHR_BS_TAIL("%[t0]")
+                     : [x] "+s"(x), [bit] "+s"(bit), [c] "=&s"(c), [t0] "=&s"(t0),
+                       [t1] "=&s"(t1), [m0] "=&s"(m0), [m1] "=&s"(m1)
+                     : [r0] "v"(rel[0]), [r1] "v"(rel[1]), [need] "s"(need)
+                     : "scc");
+    } else if constexpr (NS == 3) {
+        asm volatile(ALHR_BS_HEAD ALHR_BS_CMP(0) ALHR_BS_CMP(1) ALHR_BS_CMP(2) ALHR_BS_CNT(0)
+                     ALHR_BS_CNT(1) ALHR_BS_CNT(2)
+                     "s_add_u32 %[t0], %[t0], %[t1]\n s_add_u32 %[t0], %[t0], %[t2]\n"
+                     ALHR_BS_TAIL("%[t0]")
+                     : [x] "+s"(x), [bit] "+s"(bit), [c] "=&s"(c), [t0] "=&s"(t0),
+                       [t1] "=&s"(t1), [t2] "=&s"(t2), [m0] "=&s"(m0), [m1] "=&s"(m1),
+                       [m2] "=&s"(m2)
+                     : [r0] "v"(rel[0]), [r1] "v"(rel[1]), [r2] "v"(rel[2]), [need] "s"(need)
+                     : "scc");
+    } else {
+        asm volatile(ALHR_BS_HEAD ALHR_BS_CMP(0) ALHR_BS_CMP(1) ALHR_BS_CMP(2) ALHR_BS_CMP(3)
+                     ALHR_BS_CNT(0) ALHR_BS_CNT(1) ALHR_BS_CNT(2) ALHR_BS_CNT(3)
+                     "s_add_u32 %[t0], %[t0], %[t1]\n s_add_u32 %[t2], %[t2], %[t3]\n"
+                     "s_add_u32 %[t0], %[t0], %[t2]\n" ALHR_BS_TAIL("%[t0]")
+                     : [x] "+s"(x), [bit] "+s"(bit), [c] "=&s"(c), [t0] "=&s"(t0),
+                       [t1] "=&s"(t1), [t2] "=&s"(t2), [t3] "=&s"(t3), [m0] "=&s"(m0),
+                       [m1] "=&s"(m1), [m2] "=&s"(m2), [m3] "=&s"(m3)
+                     : [r0] "v"(rel[0]), [r1] "v"(rel[1]), [r2] "v"(rel[2]), [r3] "v"(rel[3]),
+                       [need] "s"(need)
+                     : "scc");
     }
     return x;
 }
+#undef ALHR_BS_HEAD
+#undef ALHR_BS_CMP
+#undef ALHR_BS_CNT
+#undef ALHR_BS_TAIL
 
 // Keep the best min(r, #non-empty) keys of cand[0, n) (0 = empty slot) in
 // beam[0, ...), in slot order, and return how many were kept; `inner` tells
