@@ -1,0 +1,85 @@
+"""Host-side checks of bench.py's own logic (no GPU): the one-GPU guard, the
+algorithmic byte model, the counter-file reader and the oracle baseline.
+"""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+from synth.workloads import WORKLOADS, host_inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr and p.stdout == ""
+
+
+def test_byte_model_by_hand():
+    """One query of d = 64 with window 4: 3 int32 rows, 10 int16 rows, 5 key
+    rows loaded, 20 keys selected, budget read."""
+    class Cfg:
+        d, window, max_budget = 64, 4, 96
+    stats = np.array([[3, 10, 5, 20]], dtype=np.int32)
+    d = 64
+    want = (d + 4 * d + 3 * 4 * d + 10 * 2 * d + 5 * d + 20 * 4 * d + 4 * d
+            + 4 * 96 + 4 + 4)
+    assert int(bench.bytes_per_query(stats, Cfg())[0]) == want
+    assert int(bench.bytes_per_query(stats, Cfg(), budget_read=False)[0]) == want - 4
+    # fewer selected keys than the window: only C neighbours are read
+    stats = np.array([[0, 0, 0, 2]], dtype=np.int32)
+    assert int(bench.bytes_per_query(stats, Cfg())[0]) == (
+        d + 2 * d + 2 * 4 * d + 4 * d + 4 * 96 + 4 + 4)
+
+
+def test_counter_file_is_read_only_for_the_matching_source(tmp_path, monkeypatch):
+    f = tmp_path / "counters.txt"
+    sha = bench.route_source_sha()
+    body = ("# comment: 1\nroute_source_sha: %s\nfetch_kib_per_dispatch: 10.0\n"
+            "write_kib_per_dispatch: 4.0\ncopy_fetch_factor: 2.0\ncopy_write_factor: 1.0\n")
+    f.write_text(body % sha)
+    monkeypatch.setattr(bench, "PROFILE_COUNTERS", str(f))
+    assert bench.read_traffic() == (2.0 * 10.0 + 4.0) * 1024
+    f.write_text(body % ("0" * 16))
+    assert bench.read_traffic() is None
+    f.write_text("route_source_sha: %s\nfetch_kib_per_dispatch: x\n" % sha)
+    assert bench.read_traffic() is None
+    monkeypatch.setattr(bench, "PROFILE_COUNTERS", str(tmp_path / "absent.txt"))
+    assert bench.read_traffic() is None
+
+
+def test_committed_counter_file_parses():
+    """The committed summary carries every key the reader needs (whether its
+    hash matches the current source is the bench's business)."""
+    kv = {}
+    for line in open(bench.PROFILE_COUNTERS):
+        line = line.split("#")[0].strip()
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    for k in ("route_source_sha", "fetch_kib_per_dispatch", "write_kib_per_dispatch",
+              "copy_fetch_factor", "copy_write_factor"):
+        assert k in kv, k
+    assert len(kv["route_source_sha"]) == 16
+    assert float(kv["fetch_kib_per_dispatch"]) > 0 and float(kv["write_kib_per_dispatch"]) > 0
+
+
+@pytest.mark.parametrize("threads", [1, 2])
+def test_oracle_baseline_counts_the_sample(threads):
+    w = WORKLOADS["tiny"]
+    Q, K, V, W = host_inputs(w)
+    out = bench.cpu_baseline(w, Q, K, V, W, 8, threads)
+    assert out["kind"] == "oracle" and out["unit"] == "queries/s"
+    assert out["cores"] == min(threads, w.B * w.H)
+    assert "(%d queries)" % (w.B * w.H * len(range(0, w.T, 8))) in out["sample"]
+    assert out["value"] > 0
+
+
+def test_host_cores_is_bounded():
+    assert 1 <= bench.host_cores() <= 16
