@@ -243,7 +243,7 @@ def bench_prefill(args, torch, dev):
     bud = budget.cpu().numpy() if wt is not None else np.full_like(cnt, fixed)
     queries = w.B * w.H * w.T
     out = {
-        "metric": "routed queries/sec (build+route+attend) at T=16384; % of HBM peak",
+        "metric": "routed queries/sec (build+route+attend) at T=%d; %% of HBM peak" % w.T,
         "value": queries / (ms_step * 1e-3),
         "unit": "queries/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -52,43 +52,49 @@ __device__ __forceinline__ void stage_weights(const int8_t* __restrict__ W, int 
     for (int i = threadIdx.x; i < nc * (D / 2); i += kChunk) wl[i] = w[i];
 }
 
+// Chunk totals: by linearity the sum over the chunk of W_s[c] . K[t] is
+// W_s[c] . (sum over the chunk of K[t]), so the chunk's key rows are summed
+// per column first (coalesced dword loads, one LDS reduction) and then dotted
+// with each class row: D loads per position instead of 32 class dots.  Exact
+// in int32 under the declared bounds, like every other order of this sum.
 template <int D>
 __global__ __launch_bounds__(kChunk) void k_predict_chunks(const int8_t* __restrict__ K,
                                                            const int8_t* __restrict__ W,
                                                            int32_t* __restrict__ tot, int T, int nc)
 {
-    __shared__ __align__(16) int wl[kMaxClasses * D / 2];
-    __shared__ int part[kChunk / 32][kMaxClasses + 1];
-    __shared__ int us[kChunk][kMaxClasses + 1];
+    constexpr int C4 = D / 4, RG = kChunk / C4;   // dword columns, row groups
+    __shared__ int part[RG][D + 1];
+    __shared__ int colsum[D];
     const int nch = (int)chunks_per_pair(T);
     const int pair = blockIdx.x / nch, chunk = blockIdx.x % nch;
-    stage_weights<D>(W, nc, wl);
-    __syncthreads();
-    const int t = chunk * kChunk + threadIdx.x;
-    int u[kMaxClasses];
-    if (t < T) {
-        int kw[D / 4];
-        const int* kr = reinterpret_cast<const int*>(K + ((size_t)pair * T + t) * D);
-#pragma unroll
-        for (int i = 0; i < D / 4; ++i) kw[i] = kr[i];
-        class_dots<D>(kw, wl, nc, D / 4, u);
-    } else {
-#pragma unroll
-        for (int c = 0; c < kMaxClasses; ++c) u[c] = 0;
+    const int g = threadIdx.x % C4, rg = threadIdx.x / C4;
+    const int* kr = reinterpret_cast<const int*>(K) + (size_t)pair * T * C4;
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+    for (int r = rg; r < kChunk; r += RG) {
+        const int t = chunk * kChunk + r;
+        if (t < T) {
+            const int w = kr[(size_t)t * C4 + g];
+            a0 += sbyte(w, 0);
+            a1 += sbyte(w, 1);
+            a2 += sbyte(w, 2);
+            a3 += sbyte(w, 3);
+        }
     }
-#pragma unroll
-    for (int c = 0; c < kMaxClasses; ++c) us[threadIdx.x][c] = u[c];
+    part[rg][4 * g + 0] = a0;
+    part[rg][4 * g + 1] = a1;
+    part[rg][4 * g + 2] = a2;
+    part[rg][4 * g + 3] = a3;
     __syncthreads();
-    {   // thread (segment, class) sums 32 positions
-        const int c = threadIdx.x % kMaxClasses, seg = threadIdx.x / kMaxClasses;
+    for (int j = threadIdx.x; j < D; j += kChunk) {
         int acc = 0;
-        for (int j = 0; j < 32; ++j) acc += us[seg * 32 + j][c];
-        part[seg][c] = acc;
+        for (int k = 0; k < RG; ++k) acc += part[k][j];
+        colsum[j] = acc;
     }
     __syncthreads();
     if (threadIdx.x < nc) {
+        const int8_t* ws = W + (size_t)threadIdx.x * 2 * D + D;
         int acc = 0;
-        for (int seg = 0; seg < kChunk / 32; ++seg) acc += part[seg][threadIdx.x];
+        for (int j = 0; j < D; ++j) acc += (int)ws[j] * colsum[j];
         tot[((size_t)pair * nch + chunk) * kMaxClasses + threadIdx.x] = acc;
     }
 }
