@@ -513,16 +513,17 @@ __device__ __forceinline__ void write_selection(const WaveLds& sm, int C, int ma
 }
 
 // softmax over sm.score[0, C) * scale and the weighted sum of value rows.
-// Positions outside [0, T) (possible only in caller-supplied index sets) are
-// left out of the softmax and never loaded; with none left the output is 0.
-template <int D>
+// Positions outside [0, T) (possible only in caller-supplied index sets,
+// CHECK = true) are left out of the softmax and never loaded; with none left
+// the output is 0.  Routed sets (CHECK = false) hold valid positions only.
+template <int D, bool CHECK>
 __device__ void attend_selected(WaveLds& sm, int C, int T, float scale,
                                 const float* __restrict__ values_pair, float* __restrict__ out)
 {
     constexpr int LPV = D / 4, RPV = kWave / LPV;
     const int lane = lane_id();
-    const bool ok0 = lane < C && (unsigned)sm.pos[lane] < (unsigned)T;
-    const bool ok1 = lane + kWave < C && (unsigned)sm.pos[lane + kWave] < (unsigned)T;
+    const bool ok0 = lane < C && (!CHECK || (unsigned)sm.pos[lane] < (unsigned)T);
+    const bool ok1 = lane + kWave < C && (!CHECK || (unsigned)sm.pos[lane + kWave] < (unsigned)T);
     const float a0 = ok0 ? (float)sm.score[lane] * scale : -INFINITY;
     const float a1 = ok1 ? (float)sm.score[lane + kWave] * scale : -INFINITY;
     const float mx = wave_max_f(a0 > a1 ? a0 : a1);
@@ -536,9 +537,10 @@ __device__ void attend_selected(WaveLds& sm, int C, int T, float scale,
     gbyte* vbase = uniform_base(values_pair);   // a pair's values are under 2^30 bytes
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     // kU rows per lane group in flight: their loads are issued before the
-    // first use.  A slot past C or holding a position outside [0, T) reads
-    // value row 0 and adds nothing (its row is replaced by zeros, so even a
-    // non-finite row 0 leaves the sum unchanged).
+    // first use.  A slot past C (or, CHECK, holding a position outside
+    // [0, T)) reads a valid stand-in row and adds nothing: its row is
+    // replaced by zeros and its weight is a finite softmax weight (or 0), so
+    // even a non-finite stand-in row leaves the sum unchanged.
     constexpr int kU = 4;
     for (int c0 = 0; c0 < C; c0 += kU * RPV) {
         int4 vi[kU];
@@ -547,16 +549,17 @@ __device__ void attend_selected(WaveLds& sm, int C, int T, float scale,
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int c = c0 + u * RPV + rv;
-            const int cc = c < kMaxBudget ? c : kMaxBudget - 1;
+            const int cc = c < C ? c : 0;   // slot 0 holds a selected position (C >= 1)
             const int j = sm.pos[cc];
-            ok[u] = c < C && (unsigned)j < (unsigned)T;
+            ok[u] = c < C && (!CHECK || (unsigned)j < (unsigned)T);
             wt[u] = sm.w[cc];
-            vi[u] = load16(vbase, (ok[u] ? (uint32_t)j : 0u) * (uint32_t)(4 * D) + 16u * (uint32_t)cv);
+            const uint32_t row = CHECK ? (ok[u] ? (uint32_t)j : 0u) : (uint32_t)j;
+            vi[u] = load16(vbase, row * (uint32_t)(4 * D) + 16u * (uint32_t)cv);
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             if (!ok[u]) {
-                wt[u] = 0.0f;
+                if (CHECK) wt[u] = 0.0f;
                 vi[u] = make_int4(0, 0, 0, 0);
             }
             acc.x += wt[u] * __int_as_float(vi[u].x);
@@ -615,7 +618,7 @@ __global__ __launch_bounds__(kThreads) void k_route(
         stats[qrow * 4 + 3] = C;
     }
     if constexpr (ATTEND)
-        attend_selected<D>(sm, C, T, scale, V + (size_t)pair * T * D, O + qrow * D);
+        attend_selected<D, false>(sm, C, T, scale, V + (size_t)pair * T * D, O + qrow * D);
 }
 
 // ---- attention over given index sets -------------------------------------
@@ -658,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(const int8_t* __restrict__ 
         }
     }
     wave_sync();
-    attend_selected<D>(sm, C, T, scale, V + (size_t)pair * T * D, O + qrow * D);
+    attend_selected<D, true>(sm, C, T, scale, V + (size_t)pair * T * D, O + qrow * D);
 }
 
 // ---- decode: one wave per pair, query at position pos --------------------
