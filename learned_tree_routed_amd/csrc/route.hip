@@ -171,21 +171,24 @@ __device__ __forceinline__ int score_node(const int32_t* __restrict__ nodes_pair
     return group_sum<LPR>(acc);
 }
 
-// Left-child scoring inside the descent, from the child's heap row r =
-// (T + start) >> level (exact: start is a multiple of 2^level) instead of
-// (level, start).  The lane-dependent parts of the byte offsets are computed
+// Left-child scoring inside the descent, from ts = T + start: the child's
+// heap row is r = ts >> level (exact: start is a multiple of 2^level).  The
+// lane-dependent parts of the byte offsets are computed
 // once per query: o16 = 2d * (T >> l16) + 16 s (an int16 row r starts at
 // 2d * (r + (T >> l16)) in the packed layout), okey = 16 s - T d (key row
 // r - T starts at d * (r - T); the sum wraps modulo 2^32 to the exact
 // offset).  Inactive lanes contribute 0.
 template <int D, bool MUL24>
-__device__ __forceinline__ int score_row(gbyte* nbase, gbyte* nbase_hi, gbyte* kbase, uint32_t r,
+__device__ __forceinline__ int score_row(gbyte* nbase, gbyte* nbase_hi, gbyte* kbase, uint32_t ts,
                                          int level, int l16, bool active, int s, uint32_t o16,
                                          uint32_t okey, const QueryRegs<D>& q)
 {
     constexpr int LPR = D / 16;
     int acc = 0;
     if (active) {
+        // ts = T + start; the heap row is ts >> level (level < 31 when active)
+        __builtin_assume(level >= 0 && level < 31);
+        const uint32_t r = ts >> (uint32_t)level;
         if (level > l16) {
             const uint32_t row = r * (uint32_t)(4 * D);
             int4 v[4];
@@ -458,6 +461,7 @@ __device__ int route_query(const int32_t* __restrict__ nodes_pair,
     const uint32_t okey = 16u * (uint32_t)s - (uint32_t)T * (uint32_t)D;
     const uint32_t tstart = (uint32_t)T + 0xFFFFFu;   // T + start = tstart - (lo >> 5)
     while (inner) {
+        const int ng = nb - g;   // entry i = base + g is below nb iff base < ng
         for (int base = 0; base < nb; base += RPG) {
             // i < 128 = kMaxBudget (base < nb <= 127 is a multiple of RPG,
             // which divides 128): entries past nb are read and their two
@@ -466,11 +470,10 @@ __device__ int route_query(const int32_t* __restrict__ nodes_pair,
             const uint64_t key = sm.beam[i];
             const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
             const int lv = (int)(lo & 31u);
-            const bool expand = i < nb && lv > 0;
+            const bool expand = base < ng && lv > 0;
             const int cl = lv - 1;
-            const uint32_t row = (tstart - (lo >> 5)) >> ((uint32_t)cl & 31u);
-            const int left = score_row<D, MUL24>(nbase, nbase_hi, kbase, row, cl, l16, expand, s,
-                                                 o16, okey, q);
+            const int left = score_row<D, MUL24>(nbase, nbase_hi, kbase, tstart - (lo >> 5), cl, l16,
+                                                 expand, s, o16, okey, q);
             if (STATS) {
                 cnt.tree_rows += wave_count(expand && s == 0 && cl > l16);
                 cnt.tree16_rows += wave_count(expand && s == 0 && cl > 0 && cl <= l16);
@@ -772,9 +775,8 @@ __device__ int route_query_block(const int32_t* __restrict__ nodes_pair,
             const int lv = (int)(lo & 31u);
             const bool expand = valid && lv > 0;
             const int cl = lv - 1;
-            const uint32_t row = (tstart - (lo >> 5)) >> ((uint32_t)cl & 31u);
-            const int left = score_row<D, MUL24>(nbase, nbase_hi, kbase, row, cl, l16, expand, s,
-                                                 o16, okey, q);
+            const int left = score_row<D, MUL24>(nbase, nbase_hi, kbase, tstart - (lo >> 5), cl, l16,
+                                                 expand, s, o16, okey, q);
             // children from the parent key (as in route_query); every lane of
             // the row group stores the same two keys
             if (valid) {
