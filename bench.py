@@ -5,9 +5,11 @@
 
 A step is one pass of the whole prefill path over one batch: tree build,
 budget prediction, and the fused route + attend kernel, i.e. the kernels
-alhr_forward launches, issued as the three ABI calls so that HIP events on
-the launch stream can time each kernel.  Inputs are synthetic and resident
-in HBM before the timed region.  Prints one JSON line:
+alhr_forward launches, issued as the three ABI calls.  The timed steps are
+replays of one HIP graph holding those calls; an eager loop of the same calls
+with HIP events on the launch stream between them times each kernel.  Inputs
+are synthetic and resident in HBM before the timed region.  Prints one JSON
+line:
 
   value     routed queries/s of the whole step (B * H * T queries per step)
   roofline  the fused route + attend kernel: algorithmic bytes per launch
@@ -168,6 +170,26 @@ def bench_splitter(alhr, torch, dev, w, reps=20):
             "hbm_GBps": nbytes / (ms * 1e-3) / 1e9}
 
 
+def step_calls(alhr, cfg, q, k, v, wt, nodes, budget, ws, fixed, idx, count, O):
+    """One prefill step: the kernels alhr_forward launches, as its three calls."""
+    alhr.alhr_build_tree(cfg, k, nodes)
+    if wt is not None:
+        alhr.alhr_predict_budget(cfg, q, k, wt, budget, ws)
+    alhr.alhr_route_attend(cfg, q, k, v, nodes, budget if wt is not None else None, fixed, idx,
+                           count, O)
+
+
+def capture_step(torch, fn):
+    """fn's launches captured in a HIP graph (on torch's capture stream, which
+    the binding launches on)."""
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    return graph
+
+
 def bench_prefill(args, torch, dev):
     import learned_tree_routed_amd as alhr
     from synth.workloads import WORKLOADS, host_inputs
@@ -210,9 +232,24 @@ def bench_prefill(args, torch, dev):
         step(events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    eager_ms = (t1 - t0) * 1e3 / args.steps
     kern = {name: float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
             for name, a, b in (("build_ms", 0, 1), ("predict_ms", 1, 2), ("route_attend_ms", 2, 3))}
+
+    # The timed figure: the same three calls captured once in a HIP graph and
+    # replayed, so the kernels run back to back instead of waiting on the
+    # host's launches (the eager loop above leaves ~20 us of launch gaps per
+    # step at t16k; its time is kept under diagnostics).
+    graph = capture_step(torch, lambda: step_calls(alhr, cfg, q, k, v, wt, nodes, budget, ws,
+                                                   fixed, idx, count, O))
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # the dense causal baseline on the same inputs (MFMA kernel), for the ratio
     dense_ms = None
@@ -254,7 +291,8 @@ def bench_prefill(args, torch, dev):
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "T": w.T, "d": w.d,
                    "window": cfg.window, "max_budget": cfg.max_budget,
                    "budget": ("fixed %d" % fixed) if fixed else "int8 predictor, 32 classes x 3",
-                   "queries_per_step": queries},
+                   "queries_per_step": queries,
+                   "launch": "HIP graph of build + predict + route/attend per step"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "k_route (fused route + attend)",
@@ -265,6 +303,7 @@ def bench_prefill(args, torch, dev):
             "ms": dense_ms, "routed_step_speedup": dense_ms / ms_step},
         "splitter": splitter,
         "diagnostics": {"mean_budget": float(bud.mean()), "mean_keys_per_query": float(cnt.mean()),
+                        "eager_ms_per_step": eager_ms,
                         "budget_histogram": {int(v): int(c) for v, c in
                                              zip(*np.unique(bud, return_counts=True))},
                         "mean_tree_rows_loaded_int32": float(stats[..., 0].mean()),

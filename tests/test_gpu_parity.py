@@ -408,3 +408,49 @@ def test_launches_split_by_query_range(torch_dev):
     O2 = alhr.alhr_sparse_attend(cfg, Q, K, V, out["idx"], out["count"])
     torch.cuda.synchronize()
     assert torch.equal(O2, out["O"])
+
+
+def test_graph_replays_of_a_step_match_eager(torch_dev):
+    """The bench's timed step (build + predict + route/attend captured in one
+    HIP graph): every replay, with eager work on the same buffers in between,
+    gives the eager outputs exactly, and those equal the oracle's on sampled
+    queries."""
+    import bench
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    w = WORKLOADS["t1k"]
+    Q, K, V, W = host_inputs(w, B=2, H=4)
+    w = Workload("t1k_graph", w.seed, 2, 4, w.T, w.d, w.kind)
+    cfg = w.config()
+    q, k, v, wt = to_dev(torch, dev, Q, K, V, W)
+    rows = (w.B, w.H, w.T, w.d)
+    nodes = torch.empty(rows, dtype=torch.int32, device=dev)
+    budget = torch.empty((w.B, w.H, w.T), dtype=torch.int32, device=dev)
+    idx = torch.empty((w.B, w.H, w.T, cfg.max_budget), dtype=torch.int32, device=dev)
+    count = torch.empty((w.B, w.H, w.T), dtype=torch.int32, device=dev)
+    O = torch.empty(rows, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(alhr.alhr_workspace_bytes(cfg), 256), dtype=torch.uint8, device=dev)
+    outs = (nodes, budget, idx, count, O)
+    say("eager step, t1k B2 H4")
+    bench.step_calls(alhr, cfg, q, k, v, wt, nodes, budget, ws, 0, idx, count, O)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    say("capture step in a graph")
+    graph = bench.capture_step(torch, lambda: bench.step_calls(alhr, cfg, q, k, v, wt, nodes, budget,
+                                                               ws, 0, idx, count, O))
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        # eager work on the same buffers between replays
+        alhr.alhr_build_tree(cfg, k, nodes)
+        torch.cuda.synchronize()
+        say("graph replay", rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b)
+    got = {name: t.cpu().numpy() for name, t in
+           (("nodes", nodes), ("budget", budget), ("idx", idx), ("count", count), ("O", O))}
+    ts = np.array([0, 1, 2, 5, 100, 511, 1000, 1023])
+    for (b, h) in ((0, 0), (1, 3)):
+        check_pair(w, cfg, Q, K, V, W, got, b, h, ts=ts)
