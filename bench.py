@@ -435,12 +435,21 @@ def bench_sweep(args, torch, dev):
             step([torch.cuda.Event(enable_timing=True) for _ in range(3)])
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for e in evs:
             step(e)
         torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / args.steps
         kms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        # step time from graph replays of the same calls, as in the main bench
+        graph = capture_step(torch, lambda: step_calls(alhr, cfg, Q, K, V, Wt, nodes, bud, ws, 0,
+                                                       idx, cnt, O))
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        del graph
         _, _, st = alhr.alhr_route_stats(cfg, Q, K, nodes, bud, 0)
         stats = st.cpu().numpy()
         bpl = int(bytes_per_query(stats, cfg).sum())
