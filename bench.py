@@ -3,11 +3,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload t16k]
 
-A step is one pass of the whole prefill path over one batch: tree build,
-budget prediction, and the fused route + attend kernel, i.e. the kernels
-alhr_forward launches, issued as the three ABI calls.  The timed steps are
-replays of one HIP graph holding those calls; an eager loop of the same calls
-with HIP events on the launch stream between them times each kernel.  Inputs
+A step is one pass of the whole prefill path over one batch: tree build and
+budget prediction (alhr_prepare: the two share their launches), then the
+fused route + attend kernel, i.e. the kernels alhr_forward launches, issued
+as its two ABI calls.  The timed steps are replays of one HIP graph holding
+those calls; an eager loop of the same calls with HIP events on the launch
+stream between them times each part.  Inputs
 are synthetic and resident in HBM before the timed region.  Prints one JSON
 line:
 
@@ -171,10 +172,10 @@ def bench_splitter(alhr, torch, dev, w, reps=20):
 
 
 def step_calls(alhr, cfg, q, k, v, wt, nodes, budget, ws, fixed, idx, count, O):
-    """One prefill step: the kernels alhr_forward launches, as its three calls."""
-    alhr.alhr_build_tree(cfg, k, nodes)
-    if wt is not None:
-        alhr.alhr_predict_budget(cfg, q, k, wt, budget, ws)
+    """One prefill step: the kernels alhr_forward launches, as its two calls
+    (tree + budgets in shared launches, then fused route + attend)."""
+    alhr.alhr_prepare(cfg, q, k, wt, nodes, budget if wt is not None else None,
+                      ws if wt is not None else None)
     alhr.alhr_route_attend(cfg, q, k, v, nodes, budget if wt is not None else None, fixed, idx,
                            count, O)
 
@@ -212,16 +213,14 @@ def bench_prefill(args, torch, dev):
 
     def step(ev):
         ev[0].record()
-        alhr.alhr_build_tree(cfg, k, nodes)
+        alhr.alhr_prepare(cfg, q, k, wt, nodes, budget if wt is not None else None,
+                          ws if wt is not None else None)
         ev[1].record()
-        if wt is not None:
-            alhr.alhr_predict_budget(cfg, q, k, wt, budget, ws)
-        ev[2].record()
         alhr.alhr_route_attend(cfg, q, k, v, nodes, budget if wt is not None else None, fixed,
                                idx, count, O)
-        ev[3].record()
+        ev[2].record()
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(4)]  # noqa: E731
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(3)]  # noqa: E731
     for _ in range(args.warmup):
         step(mk())
     torch.cuda.synchronize()
@@ -234,7 +233,7 @@ def bench_prefill(args, torch, dev):
     t1 = time.perf_counter()
     eager_ms = (t1 - t0) * 1e3 / args.steps
     kern = {name: float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
-            for name, a, b in (("build_ms", 0, 1), ("predict_ms", 1, 2), ("route_attend_ms", 2, 3))}
+            for name, a, b in (("prepare_ms", 0, 1), ("route_attend_ms", 1, 2))}
 
     # The timed figure: the same three calls captured once in a HIP graph and
     # replayed, so the kernels run back to back instead of waiting on the
@@ -292,7 +291,7 @@ def bench_prefill(args, torch, dev):
                    "window": cfg.window, "max_budget": cfg.max_budget,
                    "budget": ("fixed %d" % fixed) if fixed else "int8 predictor, 32 classes x 3",
                    "queries_per_step": queries,
-                   "launch": "HIP graph of build + predict + route/attend per step"},
+                   "launch": "HIP graph of prepare (build + predict) + route/attend per step"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "k_route (fused route + attend)",
@@ -426,8 +425,7 @@ def bench_sweep(args, torch, dev):
 
         def step(ev):
             ev[0].record()
-            alhr.alhr_build_tree(cfg, K, nodes)
-            alhr.alhr_predict_budget(cfg, Q, K, Wt, bud, ws)
+            alhr.alhr_prepare(cfg, Q, K, Wt, nodes, bud, ws)
             ev[1].record()
             alhr.alhr_route_attend(cfg, Q, K, V, nodes, bud, 0, idx, cnt, O)
             ev[2].record()

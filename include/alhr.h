@@ -105,12 +105,12 @@ typedef struct alhr_config {
     float scale;             /* softmax scale, normally fl32(1/sqrt(d))       */
 } alhr_config;
 
-/* Bytes of scratch that alhr_predict_budget / alhr_forward need (a multiple
- * of 256; 0 if cfg is invalid). */
-
 /* Number of tree levels stored as int16 rows (see `nodes` above), or -1 if
  * cfg is invalid. */
 int32_t alhr_tree_int16_levels(const alhr_config *cfg);
+
+/* Bytes of scratch that alhr_predict_budget / alhr_prepare / alhr_forward
+ * need (a multiple of 256; 0 if cfg is invalid). */
 size_t alhr_workspace_bytes(const alhr_config *cfg);
 
 /* Tree of key sums (README, opening paragraph and "Inference stage": one
@@ -128,6 +128,16 @@ alhr_status alhr_predict_budget(const alhr_config *cfg, const int8_t *Q,
                                 const int8_t *K, const int8_t *W,
                                 int32_t *budget, void *ws, size_t ws_bytes,
                                 void *stream);
+
+/* alhr_build_tree followed by alhr_predict_budget (same citations, same
+ * results, same argument rules), with the two steps sharing their launches:
+ * they are independent, so each launch runs one build pass beside one
+ * predictor pass.  W NULL: the tree only (budget and ws are then unused and
+ * may be NULL).  alhr_forward prepares this way. */
+alhr_status alhr_prepare(const alhr_config *cfg, const int8_t *Q,
+                         const int8_t *K, const int8_t *W, int32_t *nodes,
+                         int32_t *budget, void *ws, size_t ws_bytes,
+                         void *stream);
 
 /* Routing (README "Inference stage" and "Training stage"): for each query t
  * with budget B_t (budget[t], or fixed_budget when budget is NULL; values

@@ -24,7 +24,7 @@ __all__ = [
     "alhr_route_stats", "alhr_sparse_attend", "alhr_route_attend", "alhr_forward",
     "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_dense_attend",
     "alhr_status_string", "alhr_last_error", "alhr_version", "alhr_tree_int16_levels",
-    "alhr_split_qk", "alhr_append_decode", "SplitConfig", "EXPORTED",
+    "alhr_split_qk", "alhr_append_decode", "alhr_prepare", "SplitConfig", "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +36,7 @@ EXPORTED = (
     "alhr_route_stats", "alhr_sparse_attend", "alhr_route_attend", "alhr_forward",
     "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_dense_attend",
     "alhr_status_string", "alhr_last_error", "alhr_version", "alhr_tree_int16_levels",
-    "alhr_split_qk", "alhr_append_decode",
+    "alhr_split_qk", "alhr_append_decode", "alhr_prepare",
 )
 
 STATUS = {0: "ALHR_OK", -1: "ALHR_ERR_ARG", -2: "ALHR_ERR_OVERFLOW", -3: "ALHR_ERR_DEVICE",
@@ -136,6 +136,7 @@ def load():
         "alhr_workspace_bytes": ([cfgp], sz),
         "alhr_build_tree": ([cfgp, P, P, P], C.c_int),
         "alhr_predict_budget": ([cfgp, P, P, P, P, P, sz, P], C.c_int),
+        "alhr_prepare": ([cfgp, P, P, P, P, P, P, sz, P], C.c_int),
         "alhr_route": ([cfgp, P, P, P, P, i32, P, P, P], C.c_int),
         "alhr_route_stats": ([cfgp, P, P, P, P, i32, P, P, P, P], C.c_int),
         "alhr_sparse_attend": ([cfgp, P, P, P, P, P, P, P], C.c_int),
@@ -263,6 +264,24 @@ def alhr_predict_budget(cfg, Q, K, W, budget=None, ws=None, stream=None):
     _call("alhr_predict_budget", C.byref(cfg.c()), _ptr(Q), _ptr(K), _ptr(W), _ptr(budget),
           _ptr(ws), nbytes, _stream(stream))
     return budget
+
+
+def alhr_prepare(cfg, Q, K, W=None, nodes=None, budget=None, ws=None, stream=None):
+    """Tree and (W given) budgets in shared launches; returns (nodes, budget)."""
+    torch = _torch()
+    rows, per_q, _ = _shapes(cfg)
+    _check("K", K, torch.int8, rows)
+    nodes = _out(nodes, "nodes", torch.int32, rows, K.device)
+    nbytes = 0
+    if W is not None:
+        _check("Q", Q, torch.int8, rows, K.device)
+        _check("W", W, torch.int8, (cfg.n_classes, 2 * cfg.d), K.device)
+        budget = _out(budget, "budget", torch.int32, per_q, K.device)
+        ws, nbytes = _workspace(cfg, ws, K.device)
+    _call("alhr_prepare", C.byref(cfg.c()), _ptr(Q), _ptr(K), _ptr(W), _ptr(nodes),
+          _ptr(budget if W is not None else None), _ptr(ws if W is not None else None), nbytes,
+          _stream(stream))
+    return nodes, (budget if W is not None else None)
 
 
 def _route_args(cfg, Q, K, nodes, budget, idx, count):

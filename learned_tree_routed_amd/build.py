@@ -30,8 +30,8 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
 ]
 
-SOURCES = ["api.hip", "build.hip", "predict.hip", "route.hip", "decode.hip", "dense.hip",
-           "split.hip"]
+SOURCES = ["api.hip", "build.hip", "predict.hip", "prep.hip", "route.hip", "decode.hip",
+           "dense.hip", "split.hip"]
 
 
 def _run(cmd):

@@ -191,6 +191,30 @@ alhr_status alhr_predict_budget(const alhr_config* cfg, const int8_t* Q, const i
     return device_status(fn, alhr::launch_predict(s, Q, K, W, budget, ws, as_stream(stream)));
 }
 
+alhr_status alhr_prepare(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
+                         const int8_t* W, int32_t* nodes, int32_t* budget, void* ws,
+                         size_t ws_bytes, void* stream)
+{
+    const char* fn = "alhr_prepare";
+    alhr::Shape s;
+    if (alhr_status st = check_config(fn, cfg, &s)) return st;
+    ALHR_NEED_PTR(K);
+    ALHR_NEED_PTR(nodes);
+    if (W) {
+        ALHR_NEED_PTR(Q);
+        ALHR_NEED_PTR(W);
+        ALHR_NEED_PTR(budget);
+        const size_t need = alhr::predict_ws_bytes(s);
+        if (!ws || ws_bytes < need || !aligned16(ws))
+            return fail(ALHR_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu%s)", fn,
+                        need, ws_bytes, ws ? "" : ", NULL");
+    }
+    (void)hipGetLastError();
+    hipStream_t st = as_stream(stream);
+    return device_status(fn, W ? alhr::launch_prep(s, Q, K, W, nodes, budget, ws, st)
+                               : alhr::launch_build(s, K, nodes, st));
+}
+
 static alhr_status route_common(const char* fn, const alhr_config* cfg, const int8_t* Q,
                                 const int8_t* K, const float* V, const int32_t* nodes,
                                 const int32_t* budget, int32_t fixed_budget, int32_t* idx,
@@ -291,8 +315,9 @@ alhr_status alhr_forward(const alhr_config* cfg, const int8_t* Q, const int8_t* 
     }
     hipStream_t st = as_stream(stream);
     (void)hipGetLastError();
-    hipError_t e = alhr::launch_build(s, K, nodes, st);
-    if (e == hipSuccess && W) e = alhr::launch_predict(s, Q, K, W, budget, ws, st);
+    // tree and budgets share their launches (alhr_prepare)
+    hipError_t e = W ? alhr::launch_prep(s, Q, K, W, nodes, budget, ws, st)
+                     : alhr::launch_build(s, K, nodes, st);
     if (e == hipSuccess)
         e = alhr::launch_route(s, Q, K, V, nodes, W ? budget : nullptr, fixed_budget, idx, count,
                                O, nullptr, st);

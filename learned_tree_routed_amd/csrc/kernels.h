@@ -25,6 +25,13 @@ struct Shape {
 size_t predict_ws_bytes(const Shape& s);
 
 hipError_t launch_build(const Shape& s, const int8_t* K, int32_t* nodes, hipStream_t st);
+// The build passes from tree level in_level up (in_level = 0: from the keys).
+hipError_t launch_build_from(const Shape& s, const int8_t* K, int32_t* nodes, int in_level,
+                             hipStream_t st);
+// Tree build and budget prediction sharing their launches (prep.hip); ws as
+// for launch_predict.
+hipError_t launch_prep(const Shape& s, const int8_t* Q, const int8_t* K, const int8_t* W,
+                       int32_t* nodes, int32_t* budget, void* ws, hipStream_t st);
 
 hipError_t launch_predict(const Shape& s, const int8_t* Q, const int8_t* K, const int8_t* W,
                           int32_t* budget, void* ws, hipStream_t st);

@@ -155,6 +155,27 @@ def test_workspace_checks():
 
 
 @pytestmark_cpu
+def test_prepare_argument_checks():
+    c = cfg()
+    lib = alhr.load()
+    cc = C.byref(c.c())
+    need = alhr.alhr_workspace_bytes(c)
+    prep = lib.alhr_prepare
+    # K and nodes always; Q, budget and a large enough workspace when W is given
+    assert prep(cc, P0, NULL, P0, P0, P0, P0, need, NULL) == -1
+    assert prep(cc, P0, P0, P0, NULL, P0, P0, need, NULL) == -1
+    assert prep(cc, NULL, P0, P0, P0, P0, P0, need, NULL) == -1
+    assert prep(cc, P0, P0, P0, P0, NULL, P0, need, NULL) == -1
+    assert prep(cc, P0, P0, P_ODD, P0, P0, P0, need, NULL) == -1
+    assert prep(cc, P0, P0, P0, P0, P0, P0, need - 256, NULL) == -5
+    assert prep(cc, P0, P0, P0, P0, P0, NULL, need, NULL) == -5
+    c.T = 1000
+    assert prep(C.byref(c.c()), P0, P0, P0, P0, P0, P0, need, NULL) == -1
+    # a valid call reaches the device (W NULL: the tree only, Q and ws unused)
+    assert prep(cc, NULL, P0, NULL, P0, NULL, NULL, 0, NULL) == -3
+
+
+@pytestmark_cpu
 def test_decode_and_append_argument_checks():
     c = alhr.Config(batch=2, heads=2, T=1024, d=128)
     lib = alhr.load()

@@ -431,6 +431,8 @@ def test_graph_replays_of_a_step_match_eager(torch_dev):
     O = torch.empty(rows, dtype=torch.float32, device=dev)
     ws = torch.empty(max(alhr.alhr_workspace_bytes(cfg), 256), dtype=torch.uint8, device=dev)
     outs = (nodes, budget, idx, count, O)
+    for t in outs:   # the tail of the compact tree table is never written
+        t.zero_()
     say("eager step, t1k B2 H4")
     bench.step_calls(alhr, cfg, q, k, v, wt, nodes, budget, ws, 0, idx, count, O)
     torch.cuda.synchronize()
@@ -454,3 +456,47 @@ def test_graph_replays_of_a_step_match_eager(torch_dev):
     ts = np.array([0, 1, 2, 5, 100, 511, 1000, 1023])
     for (b, h) in ((0, 0), (1, 3)):
         check_pair(w, cfg, Q, K, V, W, got, b, h, ts=ts)
+
+
+PREP_CASES = [
+    # T, d, batch, heads: one shared pass (T2, T8), two (T1024 d64: 8 + 2 levels), three
+    # build passes (T2^17 d64: 8 + 8 + 1 levels), T below one predictor chunk
+    (2, 16, 1, 3), (8, 32, 2, 1), (128, 16, 1, 2), (1024, 64, 2, 2), (4096, 128, 1, 2),
+    (2048, 256, 1, 1), (1 << 17, 64, 1, 1),
+]
+
+
+@pytest.mark.parametrize("T,d,B,H", PREP_CASES, ids=["T%d_d%d_B%d_H%d" % c for c in PREP_CASES])
+def test_prepare_equals_build_and_predict(torch_dev, T, d, B, H):
+    """alhr_prepare (tree and predictor sharing launches) writes exactly the
+    tree and budgets of alhr_build_tree + alhr_predict_budget, and the budgets
+    equal the oracle's on sampled pairs; with W NULL it builds the tree only."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    w = Workload("prep", 9, B, H, T, d, "clustered")
+    Q, K, V, W = host_inputs(w)
+    cfg = w.config()
+    q, k, wt = to_dev(torch, dev, Q, K, W)
+    say("alhr_prepare", "B%d H%d T%d d%d" % (B, H, T, d))
+    nodes, bud = alhr.alhr_prepare(cfg, q, k, wt)
+    nodes2 = alhr.alhr_build_tree(cfg, k)
+    bud2 = alhr.alhr_predict_budget(cfg, q, k, wt)
+    nodes3, none = alhr.alhr_prepare(cfg, None, k)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(bud, bud2)
+    # compare the stored rows (the tail of a compact table is never written)
+    l16 = alhr.alhr_tree_int16_levels(cfg)
+    a, b2, c = (x.cpu().numpy() for x in (nodes, nodes2, nodes3))
+    for bb in range(B):
+        for hh in range(H):
+            ref_rows = decode_tree(b2[bb, hh], l16)[1:]
+            np.testing.assert_array_equal(decode_tree(a[bb, hh], l16)[1:], ref_rows)
+            np.testing.assert_array_equal(decode_tree(c[bb, hh], l16)[1:], ref_rows)
+    ts = np.unique(np.r_[0, 1, T - 1, np.random.default_rng(T).integers(0, T, 16)])
+    for (b, h) in ((0, 0), (B - 1, H - 1)):
+        ref = oracle.pair_forward(Q[b, h], K[b, h], V[b, h], W=W, window=cfg.window,
+                                  keys_per_class=cfg.keys_per_class, max_budget=cfg.max_budget,
+                                  scale=cfg.scale, ts=ts)
+        np.testing.assert_array_equal(bud[b, h].cpu().numpy()[ts], ref["budget"])
+    check_nodes(a, K, 0, 0, cfg)
