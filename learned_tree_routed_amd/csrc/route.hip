@@ -417,17 +417,40 @@ __device__ int route_query(const int32_t* __restrict__ nodes_pair,
     const int r = C - n;
     const int m = t + 1 - n;
 
-    // neighbours m..t go to slots r.. (they follow every routed key, which is < m)
-    for (int base = 0; base < n; base += RPG) {
-        const int k = base + g;
-        const bool act = k < n;
-        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, l16, 0, m + k, act, s, q);
-        if (act && s == 0) {
-            sm.pos[r + k] = m + k;
-            sm.score[r + k] = sc;
+    // neighbours m..t go to slots r.. (they follow every routed key, which is
+    // < m).  Up to RPG of them (the usual window) are loaded first, with no
+    // branch (inactive lanes read key row t), and scored after the cover's
+    // rows are requested, so the two loads overlap.
+    int4 nv = make_int4(0, 0, 0, 0);
+    const bool near_one_pass = n <= RPG;
+    if (near_one_pass)
+        nv = load16(uniform_base(keys_pair),
+                    (uint32_t)(g < n ? m + g : t) * (uint32_t)D + 16u * (uint32_t)s);
+    auto finish_neighbours = [&]() {
+        if (near_one_pass) {
+            int acc = dot4_i8(q.qp[0], nv.x, 0);
+            acc = dot4_i8(q.qp[1], nv.y, acc);
+            acc = dot4_i8(q.qp[2], nv.z, acc);
+            acc = dot4_i8(q.qp[3], nv.w, acc);
+            const int sc = group_sum<LPR>(acc);
+            if (g < n && s == 0) {
+                sm.pos[r + g] = m + g;
+                sm.score[r + g] = sc;
+            }
+            return;
         }
-    }
+        for (int base = 0; base < n; base += RPG) {
+            const int k = base + g;
+            const bool act = k < n;
+            const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, l16, 0, m + k, act, s, q);
+            if (act && s == 0) {
+                sm.pos[r + k] = m + k;
+                sm.score[r + k] = sc;
+            }
+        }
+    };
     if (r == 0) {
+        finish_neighbours();
         wave_sync();
         return C;
     }
@@ -448,6 +471,7 @@ __device__ int route_query(const int32_t* __restrict__ nodes_pair,
         }
         if (b < L && s == 0) sm.cand[L - 1 - b] = act ? make_key(sc, start, b) : 0ull;
     }
+    finish_neighbours();
     wave_sync();
     bool inner;
     int nb = select_best(sm.cand, L, r, sm.beam, inner);
