@@ -48,9 +48,17 @@ ROUTE_SOURCES = [os.path.join(ROOT, "learned_tree_routed_amd", "csrc", f)
 
 
 def route_source_sha():
+    """Hash of the route kernel's source with comments and blank lines
+    dropped, so that editing a comment does not orphan the recorded counters
+    while any change to the code does."""
+    import re
     h = hashlib.sha256()
     for p in ROUTE_SOURCES:
-        h.update(open(p, "rb").read())
+        text = open(p, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 

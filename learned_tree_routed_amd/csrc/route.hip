@@ -10,21 +10,26 @@
 // compete.  The loop ends when the beam holds only leaves.
 //
 // Mapping to gfx950:
-//  * scoring: a tree row (int32 x d) is split over d/16 lanes that each load
-//    4 x 16 B and do 16 multiply-adds; a key row (int8 x d) over the same
-//    lanes with one 16 B load and 4 packed int8 dot ops; a few xor-shuffles
-//    finish the row.  64 / (d/16) rows are scored per pass.
+//  * scoring: a tree row is split over d/16 lanes (16 columns each): an
+//    int16 row (levels 1..l16) is two 16-byte loads and eight v_dot2 per
+//    lane, an int32 row (the few top levels) four loads and sixteen 24-bit
+//    multiplies, a key row one load and four v_dot4; DPP adds finish the row.
+//    64 / (d/16) rows are scored per pass.
 //  * only the left child of an expanded node is loaded: the right child's
 //    score is the parent's minus the left's (exact in integers), which
-//    halves the gathered tree bytes.
+//    halves the gathered tree bytes.  The children's keys are derived from
+//    the parent's key, and the child's heap row is (T + start) >> level.
 //  * selection: candidates are 64-bit keys (biased score | inverted start |
-//    level) held 4 per lane; the r-th best score is found by bisection on
-//    wave ballot counts, ties at the threshold by a second bisection on the
-//    start, then a ballot prefix compacts the winners.
+//    level), up to 4 per lane; the r-th best score is found by a bitwise
+//    threshold search over wave ballot counts, written in scalar assembly
+//    (ties at the threshold by a second search on the start), then a ballot
+//    prefix compacts the winners in slot order, so the beam stays sorted by
+//    position and the final picks need no sort.
 //  * beam, candidates and the final picks live in a 4.5 KiB per-wave LDS
-//    block; the final picks are sorted by counting ranks.
+//    block.
 //  * attention reuses the leaf scores as logits: fp32 softmax, then a gather
-//    of the C value rows with d/4 lanes per row (16 B each).
+//    of the C value rows with d/4 lanes per row (16 B each), four rows per
+//    lane group in flight.
 #include "append.h"
 #include "device.h"
 #include "kernels.h"
