@@ -182,19 +182,49 @@ __device__ __forceinline__ int score_node(const int32_t* __restrict__ nodes_pair
 // once per query: o16 = 2d * (T >> l16) + 16 s (an int16 row r starts at
 // 2d * (r + (T >> l16)) in the packed layout), okey = 16 s - T d (key row
 // r - T starts at d * (r - T); the sum wraps modulo 2^32 to the exact
-// offset).  Inactive lanes contribute 0.
+// offset).  A row group is active or inactive as a whole and an inactive
+// group's sum is never used, so its lanes return whatever they hold.
+// The int16 rows (the common case) are tested first.  The first product of
+// each chain is written with saturation, which keeps it in the three-operand
+// form (no separate clear of the accumulator); no partial sum can saturate,
+// since every |q . node| is below 2^31 by the host's overflow check.
+__device__ __forceinline__ int dot2_i16_first(int a, int b)
+{
+    return __builtin_amdgcn_sdot2(__builtin_bit_cast(v2s, a), __builtin_bit_cast(v2s, b), 0, true);
+}
+__device__ __forceinline__ int dot4_i8_first(int a, int b)
+{
+    return __builtin_amdgcn_sdot4(a, b, 0, true);
+}
 template <int D, bool MUL24>
 __device__ __forceinline__ int score_row(gbyte* nbase, gbyte* nbase_hi, gbyte* kbase, uint32_t ts,
                                          int level, int l16, bool active, int s, uint32_t o16,
                                          uint32_t okey, const QueryRegs<D>& q)
 {
     constexpr int LPR = D / 16;
-    int acc = 0;
+    int acc = (int)ts;   // any value: see above
     if (active) {
         // ts = T + start; the heap row is ts >> level (level < 31 when active)
         __builtin_assume(level >= 0 && level < 31);
         const uint32_t r = ts >> (uint32_t)level;
-        if (level > l16) {
+        if ((uint32_t)(level - 1) < (uint32_t)l16) {
+            const uint32_t off = r * (uint32_t)(2 * D) + o16;
+            const int4 v0 = load16(nbase, off), v1 = load16(nbase_hi, off);
+            acc = dot2_i16_first(q.qh[0], v0.x);
+            acc = dot2_i16(q.qh[1], v0.y, acc);
+            acc = dot2_i16(q.qh[2], v0.z, acc);
+            acc = dot2_i16(q.qh[3], v0.w, acc);
+            acc = dot2_i16(q.qh[4], v1.x, acc);
+            acc = dot2_i16(q.qh[5], v1.y, acc);
+            acc = dot2_i16(q.qh[6], v1.z, acc);
+            acc = dot2_i16(q.qh[7], v1.w, acc);
+        } else if (level == 0) {
+            const int4 v = load16(kbase, r * (uint32_t)D + okey);
+            acc = dot4_i8_first(q.qp[0], v.x);
+            acc = dot4_i8(q.qp[1], v.y, acc);
+            acc = dot4_i8(q.qp[2], v.z, acc);
+            acc = dot4_i8(q.qp[3], v.w, acc);
+        } else {
             const uint32_t row = r * (uint32_t)(4 * D);
             int4 v[4];
 #pragma unroll
@@ -205,6 +235,7 @@ __device__ __forceinline__ int score_row(gbyte* nbase, gbyte* nbase_hi, gbyte* k
                 qh[j] = q.qh[j];
                 asm volatile("" : "+v"(qh[j]));
             }
+            acc = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 acc += imul<MUL24>(lo16(qh[2 * j]), v[j].x);
@@ -212,23 +243,6 @@ __device__ __forceinline__ int score_row(gbyte* nbase, gbyte* nbase_hi, gbyte* k
                 acc += imul<MUL24>(lo16(qh[2 * j + 1]), v[j].z);
                 acc += imul<MUL24>(hi16(qh[2 * j + 1]), v[j].w);
             }
-        } else if (level > 0) {
-            const uint32_t off = r * (uint32_t)(2 * D) + o16;
-            const int4 v0 = load16(nbase, off), v1 = load16(nbase_hi, off);
-            acc = dot2_i16(q.qh[0], v0.x, acc);
-            acc = dot2_i16(q.qh[1], v0.y, acc);
-            acc = dot2_i16(q.qh[2], v0.z, acc);
-            acc = dot2_i16(q.qh[3], v0.w, acc);
-            acc = dot2_i16(q.qh[4], v1.x, acc);
-            acc = dot2_i16(q.qh[5], v1.y, acc);
-            acc = dot2_i16(q.qh[6], v1.z, acc);
-            acc = dot2_i16(q.qh[7], v1.w, acc);
-        } else {
-            const int4 v = load16(kbase, r * (uint32_t)D + okey);
-            acc = dot4_i8(q.qp[0], v.x, acc);
-            acc = dot4_i8(q.qp[1], v.y, acc);
-            acc = dot4_i8(q.qp[2], v.z, acc);
-            acc = dot4_i8(q.qp[3], v.w, acc);
         }
     }
     return group_sum<LPR>(acc);
@@ -303,56 +317,60 @@ __device__ __forceinline__ uint32_t bit_search(const uint32_t (&rel)[NS], uint32
 #undef ALHR_BS_CNT
 #undef ALHR_BS_TAIL
 
-// Keep the best min(r, #non-empty) keys of cand[0, n) (0 = empty slot) in
-// beam[0, ...), in slot order, and return how many were kept; `inner` tells
-// whether any kept node is internal.  NS slots per lane (n <= 64 * NS).
+// Keep the best min(r, #non-empty) keys of cand[0, n) in beam[0, ...), in
+// slot order, and return how many were kept; `inner` tells whether any kept
+// node is internal.  NS slots per lane (n <= 64 * NS).  A slot is empty when
+// its high word is 0: a real key's high word is its score with the sign bit
+// flipped, and a score of -2^31 cannot occur (the host's overflow check keeps
+// every |q . node| below 2^31), so the low word of an empty slot is free.
 template <int NS>
 __device__ int select_best_ns(const uint64_t* cand, int n, int r, uint64_t* beam, bool& inner)
 {
     const int lane = lane_id();
     uint64_t k[NS];
+    uint32_t h[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const int sl = lane + kWave * j;
         k[j] = sl < n ? cand[sl] : 0ull;
+        h[j] = (uint32_t)(k[j] >> 32);
     }
     int nvalid = 0;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) nvalid += wave_count(k[j] != 0ull);
+    for (int j = 0; j < NS; ++j) nvalid += wave_count(h[j] != 0u);
     bool sel[NS];
     if (nvalid <= r) {
 #pragma unroll
-        for (int j = 0; j < NS; ++j) sel[j] = k[j] != 0ull;
+        for (int j = 0; j < NS; ++j) sel[j] = h[j] != 0u;
     } else {
-        uint32_t h[NS];
-        uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+        // empty slots read 0, below every real key: they drop out of the
+        // maximum, and h - 1 wraps them to the top for the minimum
+        uint32_t mx = 0u, mn1 = 0xFFFFFFFFu;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            h[j] = (uint32_t)(k[j] >> 32);   // empty slots: 0, below every real key
-            if (k[j] != 0ull) {
-                mx = h[j] > mx ? h[j] : mx;
-                mn = h[j] < mn ? h[j] : mn;
-            }
+            mx = h[j] > mx ? h[j] : mx;
+            mn1 = h[j] - 1u < mn1 ? h[j] - 1u : mn1;
         }
-        mx = wave_max_u32(mx);
-        mn = wave_min_u32(mn);
+        mx = uniform(wave_max_u32(mx));
+        const uint32_t mn = uniform(wave_min_u32(mn1)) + 1u;
         // largest threshold with at least r scores >= it: a bitwise search,
         // most significant bit first, over the scores relative to the minimum
         // (empty slots read 0 and never reach a candidate threshold >= 1)
         uint32_t rel[NS];
 #pragma unroll
-        for (int j = 0; j < NS; ++j) rel[j] = k[j] != 0ull ? h[j] - mn : 0u;
-        const uint32_t lo = uniform(mn) + bit_search<NS>(rel, uniform(mx) - uniform(mn), r);
+        for (int j = 0; j < NS; ++j) rel[j] = (h[j] > mn ? h[j] : mn) - mn;
+        const uint32_t lo = mn + bit_search<NS>(rel, mx - mn, r);
+        // lo >= mn >= 1, so every test against lo below passes real keys only
         int gt = 0, eq = 0;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
             gt += wave_count(h[j] > lo);
-            eq += wave_count(k[j] != 0ull && h[j] == lo);
+            eq += wave_count(h[j] == lo);
         }
         const int need = r - gt;
         if (need == eq) {
 #pragma unroll
-            for (int j = 0; j < NS; ++j) sel[j] = k[j] != 0ull && h[j] >= lo;
+            for (int j = 0; j < NS; ++j) sel[j] = h[j] >= lo;
         } else {
             // ties at the threshold: keep the `need` lowest starts (largest low words)
             bool tie[NS];
@@ -360,7 +378,7 @@ __device__ int select_best_ns(const uint64_t* cand, int n, int r, uint64_t* beam
             uint32_t lmx = 0u, lmn = 0xFFFFFFFFu;
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
-                tie[j] = k[j] != 0ull && h[j] == lo;
+                tie[j] = h[j] == lo;
                 l[j] = (uint32_t)k[j];
                 if (tie[j]) {
                     lmx = l[j] > lmx ? l[j] : lmx;
@@ -374,8 +392,7 @@ __device__ int select_best_ns(const uint64_t* cand, int n, int r, uint64_t* beam
             for (int j = 0; j < NS; ++j) lrel[j] = tie[j] ? l[j] - lmn : 0u;
             const uint32_t a = uniform(lmn) + bit_search<NS>(lrel, uniform(lmx) - uniform(lmn), need);
 #pragma unroll
-            for (int j = 0; j < NS; ++j)
-                sel[j] = (k[j] != 0ull && h[j] > lo) || (tie[j] && l[j] >= a);
+            for (int j = 0; j < NS; ++j) sel[j] = h[j] > lo || (tie[j] && l[j] >= a);
         }
     }
     int base = 0;
@@ -511,14 +528,14 @@ __device__ int route_query(const int32_t* __restrict__ nodes_pair,
             // children from the parent key: the left child keeps the start
             // and has level lv - 1 (low word - 1); the right child starts
             // 2^cl later (low word - 1 - 32 * 2^cl) and scores parent - left
-            // (biased high word - left).  Every lane of the row group stores
-            // the same two keys.
-            const uint64_t c0 = expand ? ((uint64_t)((uint32_t)left ^ 0x80000000u) << 32) | (lo - 1u) : key;
-            const uint64_t c1 = expand
-                ? ((uint64_t)(hi - (uint32_t)left) << 32) | (lo - 1u - (32u << ((uint32_t)cl & 31u)))
-                : 0ull;
-            sm.cand[2 * i] = c0;
-            sm.cand[2 * i + 1] = c1;
+            // (biased high word - left).  A node that is not expanded keeps
+            // its key and leaves an empty slot (high word 0).  Every lane of
+            // the row group stores the same two keys.
+            const uint32_t c0hi = expand ? (uint32_t)left ^ 0x80000000u : hi;
+            const uint32_t c1hi = expand ? hi - (uint32_t)left : 0u;
+            const uint32_t c1lo = lo - 1u - (32u << ((uint32_t)cl & 31u));
+            sm.cand[2 * i] = ((uint64_t)c0hi << 32) | (lo - (uint32_t)expand);
+            sm.cand[2 * i + 1] = ((uint64_t)c1hi << 32) | c1lo;
         }
         wave_sync();
         nb = select_best(sm.cand, 2 * nb, r, sm.beam, inner);
@@ -574,7 +591,28 @@ __device__ void attend_selected(WaveLds& sm, int C, int T, float scale,
     // replaced by zeros and its weight is a finite softmax weight (or 0), so
     // even a non-finite stand-in row leaves the sum unchanged.
     constexpr int kU = 4;
-    for (int c0 = 0; c0 < C; c0 += kU * RPV) {
+    int c0 = 0;
+    if constexpr (!CHECK) {
+        // routed sets: the whole blocks of kU * RPV slots need no tests
+        for (; c0 + kU * RPV <= C; c0 += kU * RPV) {
+            int4 vi[kU];
+            float wt[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int c = c0 + u * RPV + rv;
+                wt[u] = sm.w[c];
+                vi[u] = load16(vbase, (uint32_t)sm.pos[c] * (uint32_t)(4 * D) + 16u * (uint32_t)cv);
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                acc.x += wt[u] * __int_as_float(vi[u].x);
+                acc.y += wt[u] * __int_as_float(vi[u].y);
+                acc.z += wt[u] * __int_as_float(vi[u].z);
+                acc.w += wt[u] * __int_as_float(vi[u].w);
+            }
+        }
+    }
+    for (; c0 < C; c0 += kU * RPV) {
         int4 vi[kU];
         float wt[kU];
         bool ok[kU];
@@ -806,13 +844,15 @@ __device__ int route_query_block(const int32_t* __restrict__ nodes_pair,
             const int cl = lv - 1;
             const int left = score_row<D, MUL24>(nbase, nbase_hi, kbase, tstart - (lo >> 5), cl, l16,
                                                  expand, s, o16, okey, q);
-            // children from the parent key (as in route_query); every lane of
-            // the row group stores the same two keys
+            // children from the parent key, an empty slot (high word 0) for a
+            // node kept as it is (as in route_query); every lane of the row
+            // group stores the same two keys
             if (valid) {
-                sm.cand[2 * i] = expand ? ((uint64_t)((uint32_t)left ^ 0x80000000u) << 32) | (lo - 1u) : key;
-                sm.cand[2 * i + 1] = expand
-                    ? ((uint64_t)(hi - (uint32_t)left) << 32) | (lo - 1u - (32u << ((uint32_t)cl & 31u)))
-                    : 0ull;
+                const uint32_t c0hi = expand ? (uint32_t)left ^ 0x80000000u : hi;
+                const uint32_t c1hi = expand ? hi - (uint32_t)left : 0u;
+                const uint32_t c1lo = lo - 1u - (32u << ((uint32_t)cl & 31u));
+                sm.cand[2 * i] = ((uint64_t)c0hi << 32) | (lo - (uint32_t)expand);
+                sm.cand[2 * i + 1] = ((uint64_t)c1hi << 32) | c1lo;
             }
         }
         ncand = 2 * nb;
