@@ -323,6 +323,35 @@ __device__ __forceinline__ uint32_t bit_search(const uint32_t (&rel)[NS], uint32
 // its high word is 0: a real key's high word is its score with the sign bit
 // flipped, and a score of -2^31 cannot occur (the host's overflow check keeps
 // every |q . node| below 2^31), so the low word of an empty slot is free.
+// The kept keys k[j] (slot lane + 64 j) for which pick(high word, low word)
+// holds, compacted into beam[0, ...) in slot order; returns their number and
+// sets `inner` when one of them is internal.  Each caller passes its own
+// predicate, evaluated here on an opaque copy of the key: a lane flag
+// computed in an earlier block would be rebuilt through a vector register
+// for the ballot.  All lanes are active.
+template <int NS, typename Pick>
+__device__ __forceinline__ int compact_kept(const uint64_t (&k)[NS], uint64_t* beam, bool& inner,
+                                            Pick pick)
+{
+    int base = 0;
+    uint64_t internal = 0ull;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        uint64_t kk = k[j];
+        asm("" : "+v"(kk));
+        const uint32_t hi = (uint32_t)(kk >> 32), lo = (uint32_t)kk;
+        const bool sel = pick(hi, lo);
+        const uint64_t msk = __ballot(sel);
+        if (sel) beam[base + (int)mbcnt(msk)] = kk;
+        base += popc64(msk);
+        uint64_t deep;   // lanes whose key has level > 0 (a 32-bit test on the low word)
+        asm("v_cmp_ne_u32_e64 %0, 0, %1" : "=s"(deep) : "v"(lo & 31u));
+        internal |= msk & deep;
+    }
+    inner = internal != 0ull;
+    return base;
+}
+
 template <int NS>
 __device__ int select_best_ns(const uint64_t* cand, int n, int r, uint64_t* beam, bool& inner)
 {
@@ -338,74 +367,55 @@ __device__ int select_best_ns(const uint64_t* cand, int n, int r, uint64_t* beam
     int nvalid = 0;
 #pragma unroll
     for (int j = 0; j < NS; ++j) nvalid += wave_count(h[j] != 0u);
-    bool sel[NS];
-    if (nvalid <= r) {
-#pragma unroll
-        for (int j = 0; j < NS; ++j) sel[j] = h[j] != 0u;
-    } else {
-        // empty slots read 0, below every real key: they drop out of the
-        // maximum, and h - 1 wraps them to the top for the minimum
-        uint32_t mx = 0u, mn1 = 0xFFFFFFFFu;
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            mx = h[j] > mx ? h[j] : mx;
-            mn1 = h[j] - 1u < mn1 ? h[j] - 1u : mn1;
-        }
-        mx = uniform(wave_max_u32(mx));
-        const uint32_t mn = uniform(wave_min_u32(mn1)) + 1u;
-        // largest threshold with at least r scores >= it: a bitwise search,
-        // most significant bit first, over the scores relative to the minimum
-        // (empty slots read 0 and never reach a candidate threshold >= 1)
-        uint32_t rel[NS];
-#pragma unroll
-        for (int j = 0; j < NS; ++j) rel[j] = (h[j] > mn ? h[j] : mn) - mn;
-        const uint32_t lo = mn + bit_search<NS>(rel, mx - mn, r);
-        // lo >= mn >= 1, so every test against lo below passes real keys only
-        int gt = 0, eq = 0;
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            gt += wave_count(h[j] > lo);
-            eq += wave_count(h[j] == lo);
-        }
-        const int need = r - gt;
-        if (need == eq) {
-#pragma unroll
-            for (int j = 0; j < NS; ++j) sel[j] = h[j] >= lo;
-        } else {
-            // ties at the threshold: keep the `need` lowest starts (largest low words)
-            bool tie[NS];
-            uint32_t l[NS];
-            uint32_t lmx = 0u, lmn = 0xFFFFFFFFu;
-#pragma unroll
-            for (int j = 0; j < NS; ++j) {
-                tie[j] = h[j] == lo;
-                l[j] = (uint32_t)k[j];
-                if (tie[j]) {
-                    lmx = l[j] > lmx ? l[j] : lmx;
-                    lmn = l[j] < lmn ? l[j] : lmn;
-                }
-            }
-            lmx = wave_max_u32(lmx);
-            lmn = wave_min_u32(lmn);
-            uint32_t lrel[NS];
-#pragma unroll
-            for (int j = 0; j < NS; ++j) lrel[j] = tie[j] ? l[j] - lmn : 0u;
-            const uint32_t a = uniform(lmn) + bit_search<NS>(lrel, uniform(lmx) - uniform(lmn), need);
-#pragma unroll
-            for (int j = 0; j < NS; ++j) sel[j] = h[j] > lo || (tie[j] && l[j] >= a);
-        }
-    }
-    int base = 0;
-    bool any_inner = false;
+    if (nvalid <= r)
+        return compact_kept<NS>(k, beam, inner, [](uint32_t hk, uint32_t) { return hk != 0u; });
+    // empty slots read 0, below every real key: they drop out of the maximum,
+    // and h - 1 wraps them to the top for the minimum
+    uint32_t mx = 0u, mn1 = 0xFFFFFFFFu;
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-        const uint64_t msk = __ballot(sel[j]);
-        if (sel[j]) beam[base + (int)mbcnt(msk)] = k[j];
-        base += popc64(msk);
-        any_inner |= __ballot(sel[j] && key_level(k[j]) > 0) != 0ull;
+        mx = h[j] > mx ? h[j] : mx;
+        mn1 = h[j] - 1u < mn1 ? h[j] - 1u : mn1;
     }
-    inner = any_inner;
-    return base;
+    mx = uniform(wave_max_u32(mx));
+    const uint32_t mn = uniform(wave_min_u32(mn1)) + 1u;
+    // largest threshold with at least r scores >= it: a bitwise search, most
+    // significant bit first, over the scores relative to the minimum (empty
+    // slots read 0 and never reach a candidate threshold >= 1)
+    uint32_t rel[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) rel[j] = (h[j] > mn ? h[j] : mn) - mn;
+    const uint32_t lo = mn + bit_search<NS>(rel, mx - mn, r);
+    // lo >= mn >= 1, so every test against lo below passes real keys only
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        gt += wave_count(h[j] > lo);
+        eq += wave_count(h[j] == lo);
+    }
+    const int need = r - gt;
+    if (need == eq)
+        return compact_kept<NS>(k, beam, inner, [lo](uint32_t hk, uint32_t) { return hk >= lo; });
+    // ties at the threshold: keep the `need` lowest starts (largest low words)
+    uint32_t l[NS];
+    uint32_t lmx = 0u, lmn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        l[j] = (uint32_t)k[j];
+        if (h[j] == lo) {
+            lmx = l[j] > lmx ? l[j] : lmx;
+            lmn = l[j] < lmn ? l[j] : lmn;
+        }
+    }
+    lmx = wave_max_u32(lmx);
+    lmn = wave_min_u32(lmn);
+    uint32_t lrel[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) lrel[j] = h[j] == lo ? l[j] - lmn : 0u;
+    const uint32_t a = uniform(lmn) + bit_search<NS>(lrel, uniform(lmx) - uniform(lmn), need);
+    return compact_kept<NS>(k, beam, inner, [lo, a](uint32_t hk, uint32_t lk) {
+        return hk > lo || (hk == lo && lk >= a);
+    });
 }
 
 __device__ __forceinline__ int select_best(const uint64_t* cand, int n, int r, uint64_t* beam,
