@@ -448,7 +448,8 @@ def bench_sweep(args, torch, dev):
         # step time from graph replays of the same calls, as in the main bench
         graph = capture_step(torch, lambda: step_calls(alhr, cfg, Q, K, V, Wt, nodes, bud, ws, 0,
                                                        idx, cnt, O))
-        graph.replay()
+        for _ in range(max(1, args.warmup)):
+            graph.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -539,7 +540,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: 100 for prefill workloads, whose "
+                         "steps are sub-millisecond and which otherwise run before the GPU "
+                         "has reached its steady clocks; 3 for decode)")
     ap.add_argument("--workload", default="t16k", choices=["tiny", "t1k", "t4k", "t16k", "decode"])
     ap.add_argument("--budget-override", type=int, default=0,
                     help="fixed budget for every query instead of the predictor (context runs)")
@@ -554,6 +558,8 @@ def main():
                     help="run only a plain 1 GiB read + 1 GiB write elementwise kernel (x5), the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
+    if args.warmup is None:
+        args.warmup = 3 if args.workload == "decode" else 100
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build measures one GPU; the ALHR path shards by (batch, head) "
