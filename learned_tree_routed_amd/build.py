@@ -33,6 +33,12 @@ FLAGS = [
 SOURCES = ["api.hip", "build.hip", "predict.hip", "prep.hip", "route.hip", "decode.hip",
            "dense.hip", "split.hip"]
 
+# Per-source extra flags.  dense.hip: matrix-core accumulators and results in
+# ordinary vector registers, so the softmax and rescaling between the
+# products do not copy them out of and back into the accumulation registers
+# on every key block.
+EXTRA = {"dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def _run(cmd):
     p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -44,7 +50,7 @@ def _run(cmd):
 
 
 def _compile(src, obj):
-    return _run([HIPCC] + FLAGS + ["-c", src, "-o", obj])
+    return _run([HIPCC] + FLAGS + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj])
 
 
 def _link(objs, out):

@@ -4,18 +4,25 @@
 // article asks the comparison to use (section "接下来最该验证的不是更高压缩比").
 // O[t] = sum_{j <= t} softmax_j(scale * Q[t] . K[j]) V[j].
 //
-// One wave per block of 32 queries, streaming 32-key blocks up to the
-// diagonal with an online (running max) softmax.  Both products run on the
-// matrix cores:
+// A workgroup of 4 waves takes 4 consecutive blocks of 32 queries of one
+// pair and streams 32-key blocks up to the last block's diagonal with an
+// online (running max) softmax.  Each key block is staged once in LDS for the
+// 4 waves (K rows as they are, V transposed to d-major rows), double
+// buffered: the global loads of the next block are issued before the current
+// block's products.  Both products run on the matrix cores:
 //  * S^T = K_blk . Q_blk^T with v_mfma_i32_32x32x16_i8 (exact int32 scores);
 //    computing the transpose puts one query in each lane column, so the
 //    per-query max and sum need one cross-half exchange per block;
 //  * O^T += V_blk^T . P^T with v_mfma_f32_32x32x2_f32: the probabilities stay
 //    fp32 (tolerance 1e-4 against an fp64 reference), and the B operand of
-//    step r is the lane's own accumulator element r, so P never moves.
+//    step r is the lane's own accumulator element r, so P never moves; the A
+//    operands of four consecutive steps are four consecutive keys of one
+//    d-major V row in LDS, one 16-byte read.
 // MFMA 32x32 layouts (checked on gfx950): A lane l holds row l%32 (int8: k =
 // 8*(l/32)..+7; f32: k = l/32), B lane l holds column l%32 with the same k,
 // and C element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+#include <climits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -27,22 +34,174 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kBlk = 32;
 constexpr int kDenseWaves = 4;
+constexpr int kThreads = kDenseWaves * kWave;
 
 __device__ __forceinline__ int key_row_of(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// One staged key block: K rows (D bytes, padded to keep 16-byte rows
+// aligned) and V transposed, vt[c][j] = V[k0 + j][c], rows padded to 36
+// floats so that a lane group's 16-byte reads hit distinct banks.
 template <int D>
-__global__ __launch_bounds__(kDenseWaves * kWave) void k_dense(
-    const int8_t* __restrict__ Q, const int8_t* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, int P, int T, float scale)
+struct DenseTile {
+    static constexpr int kKs = D + 16;
+    static constexpr int kVs = kBlk + 4;
+    int8_t k[kBlk][kKs];
+    float vt[D][kVs];
+};
+
+// The global loads of one key block, one or more 16-byte chunks per thread:
+// K: 2D chunks (row j = chunk / (D/16), chunk column c = chunk % (D/16)),
+// V: 8D chunks (row j = chunk % 32, float4 column c = chunk / 32).
+template <int D>
+struct DenseStage {
+    static constexpr int kKc = (2 * D + kThreads - 1) / kThreads;
+    static constexpr int kVc = 8 * D / kThreads;
+    int4 k[kKc];
+    float4 v[kVc];
+};
+
+template <int D>
+__device__ __forceinline__ void dense_load(DenseStage<D>& st, const int8_t* __restrict__ Kp,
+                                           const float* __restrict__ Vp, int k0, int T)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < DenseStage<D>::kKc; ++u) {
+        const int ch = t + kThreads * u;
+        if (ch < 2 * D) {
+            const int j = ch / (D / 16), c = ch % (D / 16);
+            const int row = k0 + j < T ? k0 + j : T - 1;   // rows past T: finite stand-ins
+            st.k[u] = reinterpret_cast<const int4*>(Kp + (size_t)row * D)[c];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < DenseStage<D>::kVc; ++u) {
+        const int ch = t + kThreads * u;
+        const int j = ch % kBlk, c = ch / kBlk;
+        const int row = k0 + j < T ? k0 + j : T - 1;
+        st.v[u] = reinterpret_cast<const float4*>(Vp + (size_t)row * D)[c];
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void dense_store(const DenseStage<D>& st, DenseTile<D>& tile)
+{
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < DenseStage<D>::kKc; ++u) {
+        const int ch = t + kThreads * u;
+        if (ch < 2 * D) {
+            const int j = ch / (D / 16), c = ch % (D / 16);
+            *reinterpret_cast<int4*>(&tile.k[j][16 * c]) = st.k[u];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < DenseStage<D>::kVc; ++u) {
+        const int ch = t + kThreads * u;
+        const int j = ch % kBlk, c = ch / kBlk;
+        tile.vt[4 * c + 0][j] = st.v[u].x;
+        tile.vt[4 * c + 1][j] = st.v[u].y;
+        tile.vt[4 * c + 2][j] = st.v[u].z;
+        tile.vt[4 * c + 3][j] = st.v[u].w;
+    }
+}
+
+// The running-maximum slack: the maximum a query's probabilities are taken
+// against moves only when a block's maximum exceeds it by more than this
+// (natural-log units), so exp() of a logit never exceeds e^8 and the
+// accumulators are rescaled a few times per query instead of on most blocks.
+// Every choice of the reference maximum gives the same softmax.
+constexpr float kMaxSlack = 8.0f;
+
+// One key block's product for the wave: S^T on the int8 matrix cores, the
+// online softmax update and O^T += V^T P^T.  MASK: the block holds keys past
+// a query of the wave (its diagonal) or past T.
+template <int D, bool MASK>
+__device__ __forceinline__ void dense_block(const DenseTile<D>& tl, int k0, int qrow, int T,
+                                            float c1, const int64_t (&qb_op)[D / 16],
+                                            v16f (&acc)[D / 32], float& m, float& lsum)
+{
+    constexpr int NT = D / 32, NK = D / 16;
+    const int lane = lane_id(), col = lane & 31, half = lane >> 5;
+    v16i sc = (v16i){};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+        const int64_t ka = *reinterpret_cast<const int64_t*>(&tl.k[col][16 * kk + 8 * half]);
+        sc = __builtin_amdgcn_mfma_i32_32x32x16_i8(ka, qb_op[kk], sc, 0, 0, 0);
+    }
+    bool ok[16];
+    int smax = INT_MIN;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int key = k0 + key_row_of(r, lane);
+        ok[r] = !MASK || (key <= qrow && key < T);
+        const int v = ok[r] ? sc[r] : INT_MIN;
+        smax = v > smax ? v : smax;
+    }
+    const int so = __shfl_xor(smax, 32);
+    smax = so > smax ? so : smax;   // a real score: key k0 <= every query of the block
+    // logits scale * s in log2 units: c1 = scale * log2(e)
+    const float mb = (float)smax * c1;
+    const float mn = mb > m + kMaxSlack * 1.44269504f ? mb : m;
+    if (__ballot(mn != m) != 0ull) {
+        const float corr = exp2f(m - mn);   // 1 where unchanged, 0 on the first block
+        lsum *= corr;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) acc[i] *= corr;
+        m = mn;
+    }
+    float p[16];
+    float ps = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        p[r] = exp2f(__builtin_fmaf((float)sc[r], c1, -m));
+        if (MASK) p[r] = ok[r] ? p[r] : 0.0f;
+        ps += p[r];
+    }
+    lsum += ps;
+    // steps r = 4a + b use keys 8a + 4 half + b: four consecutive keys of the
+    // lane's d-major V row, one 16-byte read per (a, tile); the tiles'
+    // accumulators alternate so consecutive products are independent
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        float4 vv[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+            vv[i] = *reinterpret_cast<const float4*>(&tl.vt[32 * i + col][8 * a + 4 * half]);
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[i].x, p[4 * a + 0], acc[i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[i].y, p[4 * a + 1], acc[i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[i].z, p[4 * a + 2], acc[i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[i].w, p[4 * a + 3], acc[i], 0, 0, 0);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_dense(const int8_t* __restrict__ Q,
+                                                    const int8_t* __restrict__ K,
+                                                    const float* __restrict__ V,
+                                                    float* __restrict__ O, int P, int T,
+                                                    float scale)
 {
     constexpr int NT = D / 32;    // 32-wide output tiles along d
     constexpr int NK = D / 16;    // int8 MFMA steps along d
-    const int lane = lane_id();
+    __shared__ DenseTile<D> tiles[2];
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
     const int nqb = (T + kBlk - 1) / kBlk;
-    const int w = uniform((int)(xcd_logical_block() * kDenseWaves + threadIdx.x / kWave));
-    if (w >= P * nqb) return;
-    const int pair = w / nqb;
-    const int qb = nqb - 1 - w % nqb;        // long (late) query blocks first
+    const int ngr = (nqb + kDenseWaves - 1) / kDenseWaves;
+    const int w = (int)xcd_logical_block();
+    if (w >= P * ngr) return;                      // uniform over the workgroup
+    const int pair = w / ngr;
+    const int gr = ngr - 1 - w % ngr;              // long (late) query groups first
+    const int qb = gr * kDenseWaves + wv;          // this wave's query block (may be >= nqb)
+    const int kb_end = min(gr * kDenseWaves + kDenseWaves - 1, nqb - 1);   // uniform
     const int q0 = qb * kBlk;
     const int8_t* Qp = Q + (size_t)pair * T * D;
     const int8_t* Kp = K + (size_t)pair * T * D;
@@ -59,51 +218,36 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void k_dense(
     v16f acc[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) acc[i] = (v16f){};
-    float m = -INFINITY, lsum = 0.0f;
+    float m = -INFINITY, lsum = 0.0f;   // m: reference maximum in log2 units
+    const float c1 = scale * 1.44269504f;
 
-    for (int kb = 0; kb <= qb; ++kb) {
+    DenseStage<D> st;
+    dense_load<D>(st, Kp, Vp, 0, T);
+    dense_store<D>(st, tiles[0]);
+    __syncthreads();
+    // this wave's key blocks are 0 .. qb (its diagonal); the workgroup's go on
+    // to kb_end, and every wave takes part in staging all of them
+    const int kb_mine = qb < nqb ? qb : -1;
+    int kb = 0;
+    for (; kb <= kb_mine; ++kb) {
+        const bool more = kb < kb_end;
+        if (more) dense_load<D>(st, Kp, Vp, (kb + 1) * kBlk, T);
         const int k0 = kb * kBlk;
-        const int krow = k0 + col < T ? k0 + col : T - 1;
-        v16i s = (v16i){};
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-            const int64_t ka =
-                *reinterpret_cast<const int64_t*>(Kp + (size_t)krow * D + 16 * kk + 8 * half);
-            s = __builtin_amdgcn_mfma_i32_32x32x16_i8(ka, qb_op[kk], s, 0, 0, 0);
-        }
-        float p[16];
-        float mb = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = k0 + key_row_of(r, lane);
-            const bool ok = key <= qrow && key < T;
-            p[r] = ok ? (float)s[r] * scale : -INFINITY;
-            mb = p[r] > mb ? p[r] : mb;
-        }
-        const float mo = __shfl_xor(mb, 32);
-        mb = mo > mb ? mo : mb;
-        const float mn = m > mb ? m : mb;      // finite: key k0 <= every query of the block
-        const float corr = __expf(m - mn);
-        float ps = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            p[r] = __expf(p[r] - mn);
-            ps += p[r];
-        }
-        lsum = lsum * corr + ps;
-        m = mn;
-#pragma unroll
-        for (int i = 0; i < NT; ++i) acc[i] *= corr;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = k0 + key_row_of(r, lane);
-            const int vrow = key < T ? key : T - 1;
-            const float* vr = Vp + (size_t)vrow * D + col;
-#pragma unroll
-            for (int i = 0; i < NT; ++i)
-                acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[32 * i], p[r], acc[i], 0, 0, 0);
-        }
+        if (kb == qb || k0 + kBlk > T)
+            dense_block<D, true>(tiles[kb & 1], k0, qrow, T, c1, qb_op, acc, m, lsum);
+        else
+            dense_block<D, false>(tiles[kb & 1], k0, qrow, T, c1, qb_op, acc, m, lsum);
+        if (more) dense_store<D>(st, tiles[(kb + 1) & 1]);
+        __syncthreads();
     }
+    for (; kb <= kb_end; ++kb) {
+        if (kb < kb_end) {
+            dense_load<D>(st, Kp, Vp, (kb + 1) * kBlk, T);
+            dense_store<D>(st, tiles[(kb + 1) & 1]);
+        }
+        __syncthreads();
+    }
+    if (qb >= nqb) return;
     const float ltot = lsum + __shfl_xor(lsum, 32);
     const float inv = 1.0f / ltot;
     if (qrow < T) {
@@ -125,10 +269,10 @@ __global__ __launch_bounds__(kDenseWaves * kWave) void k_dense(
 hipError_t launch_dense(const Shape& s, const int8_t* Q, const int8_t* K, const float* V, float* O,
                         hipStream_t st)
 {
-    const uint64_t waves = (uint64_t)s.P * ((s.T + kBlk - 1) / kBlk);
-    uint64_t blocks = (waves + kDenseWaves - 1) / kDenseWaves;
-    blocks = (blocks + kXcds - 1) / kXcds * kXcds;
-    const dim3 grid((unsigned)blocks), block(kDenseWaves * kWave);
+    // one workgroup per group of kDenseWaves query blocks of a pair
+    const uint64_t groups = (uint64_t)s.P * (((s.T + kBlk - 1) / kBlk + kDenseWaves - 1) / kDenseWaves);
+    const uint64_t blocks = (groups + kXcds - 1) / kXcds * kXcds;
+    const dim3 grid((unsigned)blocks), block(kThreads);
     switch (s.d) {
         case 32: hipLaunchKernelGGL((k_dense<32>), grid, block, 0, st, Q, K, V, O, s.P, s.T, s.scale); break;
         case 64: hipLaunchKernelGGL((k_dense<64>), grid, block, 0, st, Q, K, V, O, s.P, s.T, s.scale); break;
