@@ -306,7 +306,7 @@ def bench_prefill(args, torch, dev):
                      "bytes_per_launch": bpl, "ms_per_launch": kern["route_attend_ms"]},
         "kernels_ms": kern,
         "dense_baseline": None if dense_ms is None else {
-            "kernel": "alhr_dense_attend (causal, int8 MFMA scores, fp32 MFMA values)",
+            "kernel": "alhr_dense_attend (causal, int8 MFMA scores, P.V as three bf16 MFMA products, fp32-accurate)",
             "ms": dense_ms, "routed_step_speedup": dense_ms / ms_step},
         "splitter": splitter,
         "diagnostics": {"mean_budget": float(bud.mean()), "mean_keys_per_query": float(cnt.mean()),

@@ -13,14 +13,18 @@
 //  * S^T = K_blk . Q_blk^T with v_mfma_i32_32x32x16_i8 (exact int32 scores);
 //    computing the transpose puts one query in each lane column, so the
 //    per-query max and sum need one cross-half exchange per block;
-//  * O^T += V_blk^T . P^T with v_mfma_f32_32x32x2_f32: the probabilities stay
-//    fp32 (tolerance 1e-4 against an fp64 reference), and the B operand of
-//    step r is the lane's own accumulator element r, so P never moves; the A
-//    operands of four consecutive steps are four consecutive keys of one
-//    d-major V row in LDS, one 16-byte read.
-// MFMA 32x32 layouts (checked on gfx950): A lane l holds row l%32 (int8: k =
-// 8*(l/32)..+7; f32: k = l/32), B lane l holds column l%32 with the same k,
-// and C element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+//  * O^T += V_blk^T . P^T with v_mfma_f32_32x32x16_bf16 in three products:
+//    P and V are each split into a bf16 head and a bf16 tail (x = hi + lo up
+//    to 2^-18 |x|), and hi.hi + lo.hi + hi.lo is accumulated in fp32; the
+//    dropped lo.lo term and the split residuals leave |p v| 3 * 2^-18 short at
+//    most, so each output is within 1.2e-5 * max |v| of the fp32 result
+//    (tolerance 1e-4).  The B operand is the lane's own probabilities: the 8
+//    k-slots of step s are its accumulator elements 8s .. 8s + 7, keys
+//    16s + 8g + 4 half + b for slot 4g + b, and V is staged with each d row's
+//    keys permuted to that order, so the A operand is one 16-byte read.
+// MFMA 32x32 layouts (checked on gfx950): A lane l holds row l%32 (int8 and
+// bf16: k = 8*(l/32)..+7), B lane l holds column l%32 with the same k, and C
+// element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #include <climits>
 
 #include "device.h"
@@ -31,6 +35,7 @@ namespace {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBlk = 32;
 constexpr int kDenseWaves = 4;
@@ -39,25 +44,31 @@ constexpr int kThreads = kDenseWaves * kWave;
 __device__ __forceinline__ int key_row_of(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 // One staged key block: K rows (D bytes, padded to keep 16-byte rows
-// aligned) and V transposed, vt[c][j] = V[k0 + j][c], rows padded to 36
-// floats so that a lane group's 16-byte reads hit distinct banks.
+// aligned) and V transposed to d-major rows of bf16 heads and tails,
+// vh[c][pos(j)] + vl[c][pos(j)] = V[k0 + j][c], where pos swaps bits 2 and 3
+// of the key index (the k-slot order of the bf16 products); rows are padded
+// to 40 entries so that 8 lanes' 16-byte reads hit distinct banks.
 template <int D>
 struct DenseTile {
     static constexpr int kKs = D + 16;
-    static constexpr int kVs = kBlk + 4;
+    static constexpr int kVs = 40;
     int8_t k[kBlk][kKs];
-    float vt[D][kVs];
+    uint32_t vh[D][kVs / 2];   // packed bf16 pairs
+    uint32_t vl[D][kVs / 2];
 };
+
+__device__ __forceinline__ int vt_pos(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
 
 // The global loads of one key block, one or more 16-byte chunks per thread:
 // K: 2D chunks (row j = chunk / (D/16), chunk column c = chunk % (D/16)),
-// V: 8D chunks (row j = chunk % 32, float4 column c = chunk / 32).
+// V: 4D pairs of chunks (rows 2q and 2q + 1, q = pair % 16, float4 column
+// c = pair / 16), so a thread writes whole packed bf16 pairs.
 template <int D>
 struct DenseStage {
     static constexpr int kKc = (2 * D + kThreads - 1) / kThreads;
-    static constexpr int kVc = 8 * D / kThreads;
+    static constexpr int kVc = (4 * D + kThreads - 1) / kThreads;
     int4 k[kKc];
-    float4 v[kVc];
+    float4 v0[kVc], v1[kVc];
 };
 
 template <int D>
@@ -77,10 +88,23 @@ __device__ __forceinline__ void dense_load(DenseStage<D>& st, const int8_t* __re
 #pragma unroll
     for (int u = 0; u < DenseStage<D>::kVc; ++u) {
         const int ch = t + kThreads * u;
-        const int j = ch % kBlk, c = ch / kBlk;
-        const int row = k0 + j < T ? k0 + j : T - 1;
-        st.v[u] = reinterpret_cast<const float4*>(Vp + (size_t)row * D)[c];
+        if (ch < 4 * D) {
+            const int q = ch % (kBlk / 2), c = ch / (kBlk / 2);
+            const int r0 = k0 + 2 * q < T ? k0 + 2 * q : T - 1;   // rows past T: finite stand-ins
+            const int r1 = k0 + 2 * q + 1 < T ? k0 + 2 * q + 1 : T - 1;
+            st.v0[u] = reinterpret_cast<const float4*>(Vp + (size_t)r0 * D)[c];
+            st.v1[u] = reinterpret_cast<const float4*>(Vp + (size_t)r1 * D)[c];
+        }
     }
+}
+
+// bf16 head and tail of x and y, each pair packed (x in the low half)
+__device__ __forceinline__ void split_pair(float x, float y, uint32_t& hi, uint32_t& lo)
+{
+    const __bf16 hx = (__bf16)x, hy = (__bf16)y;   // round to nearest even
+    const __bf16 lx = (__bf16)(x - (float)hx), ly = (__bf16)(y - (float)hy);
+    hi = (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
+    lo = (uint32_t)__builtin_bit_cast(uint16_t, lx) | ((uint32_t)__builtin_bit_cast(uint16_t, ly) << 16);
 }
 
 template <int D>
@@ -98,11 +122,19 @@ __device__ __forceinline__ void dense_store(const DenseStage<D>& st, DenseTile<D
 #pragma unroll
     for (int u = 0; u < DenseStage<D>::kVc; ++u) {
         const int ch = t + kThreads * u;
-        const int j = ch % kBlk, c = ch / kBlk;
-        tile.vt[4 * c + 0][j] = st.v[u].x;
-        tile.vt[4 * c + 1][j] = st.v[u].y;
-        tile.vt[4 * c + 2][j] = st.v[u].z;
-        tile.vt[4 * c + 3][j] = st.v[u].w;
+        if (ch < 4 * D) {
+            const int q = ch % (kBlk / 2), c = ch / (kBlk / 2);
+            const int w = vt_pos(2 * q) >> 1;   // keys 2q, 2q + 1 stay adjacent
+            const float a[4] = {st.v0[u].x, st.v0[u].y, st.v0[u].z, st.v0[u].w};
+            const float b[4] = {st.v1[u].x, st.v1[u].y, st.v1[u].z, st.v1[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t hi, lo;
+                split_pair(a[e], b[e], hi, lo);
+                tile.vh[4 * c + e][w] = hi;
+                tile.vl[4 * c + e][w] = lo;
+            }
+        }
     }
 }
 
@@ -159,27 +191,24 @@ __device__ __forceinline__ void dense_block(const DenseTile<D>& tl, int k0, int 
         ps += p[r];
     }
     lsum += ps;
-    // steps r = 4a + b use keys 8a + 4 half + b: four consecutive keys of the
-    // lane's d-major V row, one 16-byte read per (a, tile); the tiles'
-    // accumulators alternate so consecutive products are independent
+    // B operands: step s takes the lane's p[8s .. 8s + 7] (keys 16s + 8g +
+    // 4 half + b for k-slot 4g + b) as bf16 heads and tails
+    uint32_t ph[8], pl[8];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        float4 vv[NT];
+    for (int r = 0; r < 8; ++r) split_pair(p[2 * r], p[2 * r + 1], ph[r], pl[r]);
 #pragma unroll
-        for (int i = 0; i < NT; ++i)
-            vv[i] = *reinterpret_cast<const float4*>(&tl.vt[32 * i + col][8 * a + 4 * half]);
+    for (int s2 = 0; s2 < 2; ++s2) {
+        const bf8 bh = __builtin_bit_cast(bf8, make_uint4(ph[4 * s2], ph[4 * s2 + 1], ph[4 * s2 + 2], ph[4 * s2 + 3]));
+        const bf8 bl = __builtin_bit_cast(bf8, make_uint4(pl[4 * s2], pl[4 * s2 + 1], pl[4 * s2 + 2], pl[4 * s2 + 3]));
 #pragma unroll
-        for (int i = 0; i < NT; ++i)
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[i].x, p[4 * a + 0], acc[i], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < NT; ++i)
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[i].y, p[4 * a + 1], acc[i], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < NT; ++i)
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[i].z, p[4 * a + 2], acc[i], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < NT; ++i)
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[i].w, p[4 * a + 3], acc[i], 0, 0, 0);
+        for (int i = 0; i < NT; ++i) {
+            // keys 16 s2 + 8 half .. + 7 of the permuted row: one 16-byte read each
+            const bf8 ah = __builtin_bit_cast(bf8, *reinterpret_cast<const uint4*>(&tl.vh[32 * i + col][8 * s2 + 4 * half]));
+            const bf8 al = __builtin_bit_cast(bf8, *reinterpret_cast<const uint4*>(&tl.vl[32 * i + col][8 * s2 + 4 * half]));
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[i], 0, 0, 0);
+        }
     }
 }
 

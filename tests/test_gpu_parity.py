@@ -354,7 +354,9 @@ def test_dense_attention_full_size_sampled(torch_dev):
 
 def test_dense_equals_routing_with_full_budget(torch_dev):
     """With the budget covering every past key the routed path is dense
-    attention: both kernels must agree on the same inputs."""
+    attention: both kernels must agree on the same inputs.  The dense kernel
+    forms P.V from bf16 heads and tails (three products), exact to within
+    3 * 2^-18 * max|v| per output; the routed kernel is plain fp32."""
     import learned_tree_routed_amd as alhr
     torch, dev = torch_dev
     T = 64
@@ -365,7 +367,8 @@ def test_dense_equals_routing_with_full_budget(torch_dev):
     dense = alhr.alhr_dense_attend(cfg, q, k, v)
     routed = alhr.alhr_forward(cfg, q, k, v, None, fixed_budget=64)
     torch.cuda.synchronize()
-    assert (dense - routed["O"]).abs().max().item() <= 1e-5
+    bound = 3 * 2.0 ** -18 * float(np.abs(V).max()) + 2e-6   # + fp32 rounding of both sums
+    assert (dense - routed["O"]).abs().max().item() <= bound
 
 
 def test_launches_split_by_query_range(torch_dev):
