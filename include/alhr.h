@@ -242,6 +242,9 @@ alhr_status alhr_append_decode(const alhr_config *cfg, int32_t pos,
  * README's result tables compare against (dense teacher rows) and the
  * optimised dense kernel the openai-hub article asks comparisons to use:
  * O[t] = sum_{j <= t} softmax_j(scale * Q[t] . K[j]) V[j], fp32 output.
+ * Scores are exact int32; the P.V product is formed from bf16 heads and
+ * tails of P and V (three matrix-core products, fp32 accumulation), so each
+ * output is within 3 * 2^-18 * max|V| of the fp32 result.
  * Uses batch, heads, T, d and scale of cfg (d = 32, 64, 128 or 256; other
  * built sizes, and batch * heads * T >= 2^31, return ALHR_ERR_UNSUPPORTED);
  * the routing fields are checked as for the other calls but not used. */
