@@ -317,12 +317,6 @@ __device__ __forceinline__ uint32_t bit_search(const uint32_t (&rel)[NS], uint32
 #undef ALHR_BS_CNT
 #undef ALHR_BS_TAIL
 
-// Keep the best min(r, #non-empty) keys of cand[0, n) in beam[0, ...), in
-// slot order, and return how many were kept; `inner` tells whether any kept
-// node is internal.  NS slots per lane (n <= 64 * NS).  A slot is empty when
-// its high word is 0: a real key's high word is its score with the sign bit
-// flipped, and a score of -2^31 cannot occur (the host's overflow check keeps
-// every |q . node| below 2^31), so the low word of an empty slot is free.
 // The kept keys k[j] (slot lane + 64 j) for which pick(high word, low word)
 // holds, compacted into beam[0, ...) in slot order; returns their number and
 // sets `inner` when one of them is internal.  Each caller passes its own
@@ -352,6 +346,12 @@ __device__ __forceinline__ int compact_kept(const uint64_t (&k)[NS], uint64_t* b
     return base;
 }
 
+// Keep the best min(r, #non-empty) keys of cand[0, n) in beam[0, ...), in
+// slot order, and return how many were kept; `inner` tells whether any kept
+// node is internal.  NS slots per lane (n <= 64 * NS).  A slot is empty when
+// its high word is 0: a real key's high word is its score with the sign bit
+// flipped, and a score of -2^31 cannot occur (the host's overflow check keeps
+// every |q . node| below 2^31), so the low word of an empty slot is free.
 template <int NS>
 __device__ int select_best_ns(const uint64_t* cand, int n, int r, uint64_t* beam, bool& inner)
 {
