@@ -391,6 +391,8 @@ def bench_decode(args, torch, dev):
         times.append(((time.perf_counter() - t0) * 1e3, ev[0].elapsed_time(ev[1])))
     ms = float(np.mean([t[0] for t in times]))
     queries = B * H * S
+    roof = decode_roofline(alhr, torch, dev, w, cfg, K, nodes, qn, Wd, bud, cnt,
+                           float(np.mean([t[1] for t in times])))
     return {
         "metric": "routed queries/sec (append+route+attend), decode at T=2^17",
         "value": queries / (ms * 1e-3), "unit": "queries/s",
@@ -401,10 +403,60 @@ def bench_decode(args, torch, dev):
         "config": {"workload": "decode", "sequences": B, "heads": H, "T": T, "d": d,
                    "prefilled": n0, "tokens_per_step": S, "queries_per_step": queries,
                    "launch": "HIP graph of 128 fused append + decode step launches"},
+        "roofline": roof,
         "diagnostics": {"mean_keys_last_step": float(cnt.float().mean().item()),
                         "event_ms_per_step": float(np.mean([t[1] for t in times])),
                         "eager_ms_per_step": eager_ms},
     }, None
+
+
+def decode_roofline(alhr, torch, dev, w, cfg, K, nodes, qn, Wd, bud, cnt, event_ms_loop,
+                    npairs=8):
+    """Algorithmic bytes of k_decode (append + route + attend) per token step
+    over its event-timed duration.  The per-query load counts come from
+    alhr_route_stats on sampled (sequence, head) pairs of the final cache, with
+    the decode queries at their positions: a query at position p reads only
+    subtrees of [0, p] and S[p], which later appends leave unchanged, so the
+    counts are those of the decode launches.  Append bytes per pair and token:
+    the key and value rows written, each ancestor row and the running key sum
+    read and written; the predictor reads the updated sum and, once per
+    step, the shared weights."""
+    B, H, T, d, n0, S = w.B, w.H, w.T, w.d, w.n0, w.steps
+    cfg1 = w.config(batch=1, heads=1)
+    l16 = alhr.alhr_tree_int16_levels(cfg1)
+    L = T.bit_length() - 1
+    rng = np.random.default_rng(w.seed)
+    picks = rng.choice(B * H, size=min(npairs, B * H), replace=False)
+    per_query = []
+    for pidx in picks:
+        b, h = divmod(int(pidx), H)
+        Kp = K[b:b + 1, h:h + 1].contiguous()
+        Np = nodes[b:b + 1, h:h + 1].contiguous()
+        Qp = torch.zeros((1, 1, T, d), dtype=torch.int8, device=dev)
+        Qp[0, 0, n0:n0 + S] = qn[b, h]
+        bp = alhr.alhr_predict_budget(cfg1, Qp, Kp, Wd)
+        _, cp, st = alhr.alhr_route_stats(cfg1, Qp, Kp, Np, bp, 0)
+        torch.cuda.synchronize()
+        # the last decode step of this pair must match what the decode launch chose
+        last = n0 + S - 1
+        assert int(bp[0, 0, last]) == int(bud[b, h]) and int(cp[0, 0, last]) == int(cnt[b, h]), \
+            "route_stats disagrees with the decode launch at pair (%d, %d)" % (b, h)
+        sel = st[0, 0, n0:n0 + S].cpu().numpy()
+        per_query.append(bytes_per_query(sel, cfg, budget_read=True))
+        del Kp, Np, Qp
+    route_b = float(np.mean(np.concatenate(per_query)))
+    anc = sum((2 * d if lvl <= l16 else 4 * d) for lvl in range(1, L + 1))
+    append_b = d + 4 * d + 2 * anc + 2 * 4 * d
+    # the predictor weights are shared by every query of the step: counted once
+    bytes_token = (route_b + append_b) * B * H + cfg.n_classes * 2 * d
+    ms_token = event_ms_loop / S
+    achieved = bytes_token / (ms_token * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "k_decode (append + route + attend, one launch per token)",
+            "bytes_per_launch": bytes_token, "ms_per_launch": ms_token,
+            "sample": "load counts of the %d decode queries of %d sampled pairs "
+                      "(alhr_route_stats on the final cache)" % (S * len(picks), len(picks))}
 
 
 def bench_sweep(args, torch, dev):
