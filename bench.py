@@ -97,6 +97,25 @@ def bytes_per_query(stats, cfg, budget_read=True):
     return b
 
 
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def dense_summary(w, dense_ms, step_ms):
+    """The dense causal baseline's time and its matrix-core roofline: per
+    (query, past key) pair 2d int8 ops for the score and, for P.V, three bf16
+    products of 2d flops each (heads and tails of P and V), against the bf16
+    dense peak (the int8 score work is a thirtieth of it and left out)."""
+    pairs = w.B * w.H * w.T * (w.T + 1) / 2
+    bf16_flops = 3 * 2 * w.d * pairs
+    achieved = bf16_flops / (dense_ms * 1e-3) / 1e12
+    return {"kernel": "alhr_dense_attend (causal, int8 MFMA scores, P.V as three bf16 MFMA "
+                      "products, fp32-accurate)",
+            "ms": dense_ms, "routed_step_speedup": dense_ms / step_ms,
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
+                         "fp32_equivalent_tflops": achieved / 3}}
+
+
 def host_cores():
     """CPUs this process may run on, at most 16 (one GPU's share of a node)."""
     try:
@@ -305,9 +324,7 @@ def bench_prefill(args, torch, dev):
                      "kernel": "k_route (fused route + attend)",
                      "bytes_per_launch": bpl, "ms_per_launch": kern["route_attend_ms"]},
         "kernels_ms": kern,
-        "dense_baseline": None if dense_ms is None else {
-            "kernel": "alhr_dense_attend (causal, int8 MFMA scores, P.V as three bf16 MFMA products, fp32-accurate)",
-            "ms": dense_ms, "routed_step_speedup": dense_ms / ms_step},
+        "dense_baseline": None if dense_ms is None else dense_summary(w, dense_ms, ms_step),
         "splitter": splitter,
         "diagnostics": {"mean_budget": float(bud.mean()), "mean_keys_per_query": float(cnt.mean()),
                         "eager_ms_per_step": eager_ms,

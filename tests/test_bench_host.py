@@ -83,3 +83,15 @@ def test_oracle_baseline_counts_the_sample(threads):
 
 def test_host_cores_is_bounded():
     assert 1 <= bench.host_cores() <= 16
+
+
+def test_dense_roofline_by_hand():
+    """Two pairs of T = 4, d = 32: 2 * 10 (query, past key) pairs, three bf16
+    products of 2d flops each; 1 ms."""
+    class W:
+        B, H, T, d = 1, 2, 4, 32
+    out = bench.dense_summary(W(), 1.0, 0.5)
+    flops = 3 * 2 * 32 * 2 * 10
+    assert out["roofline"]["achieved"] == pytest.approx(flops / 1e-3 / 1e12)
+    assert out["roofline"]["frac"] == pytest.approx(out["roofline"]["achieved"] / 2500.0)
+    assert out["routed_step_speedup"] == 2.0
