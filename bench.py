@@ -49,9 +49,11 @@ ROUTE_SOURCES = [os.path.join(ROOT, "learned_tree_routed_amd", "csrc", f)
 
 def route_source_sha():
     """Hash of the route kernel's source with comments and blank lines
-    dropped, so that editing a comment does not orphan the recorded counters
-    while any change to the code does."""
+    dropped, and of the extra compiler flags route.hip is built with, so that
+    editing a comment does not orphan the recorded counters while any change
+    to the code or to how it is compiled does."""
     import re
+    from learned_tree_routed_amd.build import EXTRA
     h = hashlib.sha256()
     for p in ROUTE_SOURCES:
         text = open(p, encoding="utf-8").read()
@@ -59,6 +61,9 @@ def route_source_sha():
         text = re.sub(r"//[^\n]*", "", text)
         lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
         h.update("\n".join(lines).encode())
+    flags = EXTRA.get("route.hip", [])
+    if flags:
+        h.update(("\nflags: " + " ".join(flags)).encode())
     return h.hexdigest()[:16]
 
 
