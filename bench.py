@@ -67,6 +67,36 @@ def route_source_sha():
     return h.hexdigest()[:16]
 
 
+PROFILE_SQ = os.path.join(ROOT, "profiles", "route_attend_t16k_sq_counters.txt")
+SIMDS, CLOCK_GHZ = 1024, 2.4   # MI355X: 256 CUs x 4 SIMDs, peak engine clock
+
+
+def read_issue(kernel_ms, waves):
+    """The route kernel's vector and scalar instruction issue against the
+    chip's issue capacity (a wave64 VALU or SALU instruction takes a SIMD's
+    issue slot for 4 cycles), from the committed SQ counter summary, or None
+    when absent or taken on other kernel source.  The kernel's working set is
+    cache resident, so this, not HBM, is what bounds it."""
+    if not os.path.exists(PROFILE_SQ):
+        return None
+    sha, per = None, {}
+    for line in open(PROFILE_SQ):
+        if "route_source_sha" in line:
+            sha = line.split("route_source_sha")[1].split()[0]
+        parts = line.lstrip("# ").split()
+        if len(parts) >= 2 and parts[0] in ("SQ_INSTS_VALU", "SQ_INSTS_SALU"):
+            try:
+                per[parts[0]] = float(parts[1])
+            except ValueError:
+                return None
+    if sha != route_source_sha() or len(per) != 2:
+        return None
+    cap = kernel_ms * 1e-3 * CLOCK_GHZ * 1e9 * SIMDS / 4   # wave64 instructions per SIMD slot
+    return {"valu_per_query": per["SQ_INSTS_VALU"], "salu_per_query": per["SQ_INSTS_SALU"],
+            "valu_issue_frac": per["SQ_INSTS_VALU"] * waves / cap,
+            "salu_issue_frac": per["SQ_INSTS_SALU"] * waves / cap}
+
+
 def read_traffic(bytes_unit=1024):
     """HBM bytes per launch of the route kernel from the committed counter
     summary, or None when absent or taken on other kernel source."""
@@ -306,7 +336,9 @@ def bench_prefill(args, torch, dev):
     stats = st.cpu().numpy()
     bpl = int(bytes_per_query(stats, cfg, wt is not None).sum())
     achieved = bpl / (kern["route_attend_ms"] * 1e-3) / 1e9
-    traffic = read_traffic() if (args.workload == "t16k" and not args.budget_override) else None
+    counted = args.workload == "t16k" and not args.budget_override
+    traffic = read_traffic() if counted else None
+    issue = read_issue(kern["route_attend_ms"], w.B * w.H * w.T) if counted else None
     cnt = count.cpu().numpy()
     bud = budget.cpu().numpy() if wt is not None else np.full_like(cnt, fixed)
     queries = w.B * w.H * w.T
@@ -327,7 +359,8 @@ def bench_prefill(args, torch, dev):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "k_route (fused route + attend)",
-                     "bytes_per_launch": bpl, "ms_per_launch": kern["route_attend_ms"]},
+                     "bytes_per_launch": bpl, "ms_per_launch": kern["route_attend_ms"],
+                     "issue": issue},
         "kernels_ms": kern,
         "dense_baseline": None if dense_ms is None else dense_summary(w, dense_ms, ms_step),
         "splitter": splitter,

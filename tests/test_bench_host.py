@@ -95,3 +95,23 @@ def test_dense_roofline_by_hand():
     assert out["roofline"]["achieved"] == pytest.approx(flops / 1e-3 / 1e12)
     assert out["roofline"]["frac"] == pytest.approx(out["roofline"]["achieved"] / 2500.0)
     assert out["routed_step_speedup"] == 2.0
+
+
+def test_issue_file_is_read_only_for_the_matching_source(tmp_path, monkeypatch):
+    f = tmp_path / "sq.txt"
+    body = ("# kernel source: route_source_sha %s\n#\n#   SQ_INSTS_VALU   2000   2100\n"
+            "#   SQ_INSTS_SALU   1000   1900\n")
+    f.write_text(body % bench.route_source_sha())
+    monkeypatch.setattr(bench, "PROFILE_SQ", str(f))
+    out = bench.read_issue(1.0, 1024)
+    # 1 ms at 2.4 GHz on 1024 SIMDs, 4 cycles per wave64 instruction
+    cap = 1e-3 * 2.4e9 * 1024 / 4
+    assert out["valu_per_query"] == 2000 and out["salu_per_query"] == 1000
+    assert out["valu_issue_frac"] == pytest.approx(2000 * 1024 / cap)
+    f.write_text(body % ("0" * 16))
+    assert bench.read_issue(1.0, 1024) is None
+
+
+def test_committed_sq_file_parses():
+    txt = open(bench.PROFILE_SQ).read()
+    assert "route_source_sha" in txt and "SQ_INSTS_VALU" in txt and "SQ_INSTS_SALU" in txt
