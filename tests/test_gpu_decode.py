@@ -164,12 +164,17 @@ def test_decode_small_every_step(torch_dev, d, fixed, fused):
     for (b, h) in pairs:
         np.testing.assert_array_equal(decode_tree(rebuilt[b, h].cpu().numpy(), l16),
                                       decode_tree(nodes[b, h].cpu().numpy(), l16))
-    # and the decode rows equal the prefill rows of the same positions
+    # and every step's rows equal the prefill rows of the same positions on
+    # the final cache: a query at position p reads only subtrees of [0, p]
+    # and the key sum up to p, which later appends leave unchanged (the
+    # decode bench's load counts rest on this)
     full = alhr.alhr_forward(cfg, Qh, Kh, Vh, Wd, fixed_budget=fixed)
     torch.cuda.synchronize()
+    f_idx, f_cnt = full["idx"].cpu().numpy(), full["count"].cpu().numpy()
     for (b, h) in pairs:
-        last = got[(b, h)][-1]
-        np.testing.assert_array_equal(last[1], full["idx"][b, h, T - 1].cpu().numpy())
+        for s_, row in enumerate(got[(b, h)]):
+            np.testing.assert_array_equal(row[1], f_idx[b, h, n0 + s_])
+            assert int(row[2]) == int(f_cnt[b, h, n0 + s_])
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["two_launches", "fused"])
