@@ -3,7 +3,8 @@
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke``
 and by the CPU-baseline leg of ``bench.py``; never by the GPU library or its
 Python binding.  The oracle is plain single-threaded C (gcc), exact int64 for
-every integer step and fp64 for attention.
+every integer step; attention logits are fp32 products of the exact score and
+the fp32 scale, the softmax and weighted sum fp64.
 
 Each function works on one (batch, head) pair with host numpy arrays:
     build_tree(K)            -> int64 [T, d] heap table (row 0 unused)
@@ -14,6 +15,9 @@ Each function works on one (batch, head) pair with host numpy arrays:
     pair_forward(...)        -> dict of per-query outputs
     pair_budgets(Q, K, W)    -> int32 [T] predicted budgets
     append(p, k, v, K, V, nodes, prefix)       (in place)
+
+ALHR_ORACLE_LIB, when set, names another build of the same source to load
+(the sanitizer build of ``build_sanitized``).
 """
 from __future__ import annotations
 
@@ -61,13 +65,26 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized(out_path: str) -> str:
+    """The same source built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (any finding aborts), for running the pin tests under the sanitizers: load
+    it through ALHR_ORACLE_LIB with the ASan runtime preloaded."""
+    subprocess.check_call(["gcc", "-O1", "-g", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+                           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                           "-fno-omit-frame-pointer", "-o", out_path, _SRC, "-lm"])
+    return out_path
+
+
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build(force=True)
-    lib = C.CDLL(_LIB)
+    path = os.environ.get("ALHR_ORACLE_LIB")
+    if not path:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+    lib = C.CDLL(path)
     P = C.c_void_p
     i32, i64, dbl = C.c_int32, C.c_int64, C.c_double
     lib.alhr_ref_build_tree.argtypes = [i32, i32, P, P]

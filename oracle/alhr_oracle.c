@@ -42,8 +42,9 @@
  * int8 by a rounding right shift and a symmetric clamp.
  *
  * Arithmetic.  Every integer quantity (node sums, prefix sums, scores,
- * predictor logits) is an exact int64.  Attention logits, softmax and the
- * weighted sum are computed in fp64 and rounded to fp32 once at the end.
+ * predictor logits) is an exact int64.  An attention logit is the fp32
+ * product of the score (exact in fp32) and the fp32 scale; the softmax and
+ * the weighted sum are computed in fp64 and rounded to fp32 once at the end.
  *
  * Layout of the tree table (per (batch, head) pair, T = 2^L positions):
  * node (level l, index p) covers keys [p*2^l, (p+1)*2^l); for l >= 1 it is
@@ -302,18 +303,25 @@ int32_t alhr_ref_route(int32_t T, int32_t d, int32_t window, int32_t t,
 
 /* ---------------------------------------------------------------- O9 ---- */
 /* Softmax attention over the selected keys (README "Inference stage"):
- * a_j = scale * (q . K[j]); out = sum_j e^{a_j - max} V[j] / sum_j e^{a_j - max},
- * all in fp64, rounded to fp32 once. */
+ * the logit of key j is a_j = fl32(fl32(q . K[j]) * scale), i.e. the exact
+ * integer score rounded to fp32 (exact while |q . K[j]| < 2^24, which the
+ * int8 inputs guarantee for d <= 256) times the fp32 scale, rounded to fp32;
+ * then out = sum_j e^{a_j - max} V[j] / sum_j e^{a_j - max} in fp64, rounded
+ * to fp32 once.  `scale` must be an fp32 value (it is converted exactly). */
 int alhr_ref_attend(int32_t d, int32_t C, const int32_t *idx, const int8_t *q,
                     const int8_t *K, const float *V, double scale, float *out)
 {
     if (d < 1 || C < 1 || !idx || !q || !K || !V || !out) return REF_ERR_ARG;
+    const float scale32 = (float)scale;
+    if ((double)scale32 != scale) return REF_ERR_ARG;
     double *a = (double *)malloc(sizeof(double) * (size_t)C);
     double *acc = (double *)calloc((size_t)d, sizeof(double));
     if (!a || !acc) { free(a); free(acc); return REF_ERR_NOMEM; }
     double mx = -INFINITY;
     for (int32_t j = 0; j < C; ++j) {
-        a[j] = (double)dot_q_key(d, q, K + (int64_t)idx[j] * d) * scale;
+        const float s32 = (float)dot_q_key(d, q, K + (int64_t)idx[j] * d);
+        const float a32 = s32 * scale32;
+        a[j] = (double)a32;
         if (a[j] > mx) mx = a[j];
     }
     double z = 0.0;

@@ -105,7 +105,29 @@ def test_budget_ties_go_to_lowest_class_and_caps_hold():
     assert oracle.budget(q, s, W)[0] == 3
 
 
+@pytest.mark.parametrize("T,d,kpc,cap", [(256, 16, 3, 96), (64, 8, 4, 96), (128, 32, 3, 40),
+                                          (2, 16, 3, 96)])
+def test_pair_budgets_match_brute_force(T, d, kpc, cap):
+    """Every query's budget from a brute-force inclusive prefix (numpy cumsum)
+    and a first-maximum argmax over the class logits; an exclusive prefix, an
+    S[t-1] offset or a last-maximum tie rule fails this."""
+    r = np.random.default_rng(T + d + kpc)
+    K = r.integers(-8, 9, size=(T, d)).astype(np.int8)
+    Q = r.integers(-9, 10, size=(T, d)).astype(np.int8)
+    W = r.integers(-4, 5, size=(32, 2 * d)).astype(np.int8)
+    W[5] = W[3]                      # two identical classes: ties must go to class 3
+    S = np.cumsum(K.astype(np.int64), axis=0)
+    z = Q.astype(np.int64) @ W[:, :d].T.astype(np.int64) + S @ W[:, d:].T.astype(np.int64)
+    expect = np.minimum(kpc * (np.argmax(z, axis=1) + 1), cap)
+    got = oracle.pair_budgets(Q, K, W, keys_per_class=kpc, max_budget=cap)
+    np.testing.assert_array_equal(got, expect)
+    V = np.zeros((T, d), np.float32)
+    full = oracle.pair_forward(Q, K, V, W=W, keys_per_class=kpc, max_budget=cap, cap=max(cap, 96))
+    np.testing.assert_array_equal(full["budget"], expect)
+
+
 # ---------------------------------------------------------------- O4 - O8 ---
+
 def route_all(K, Q, budgets, window=4, cap=96):
     nodes = oracle.build_tree(K)
     out = []
@@ -273,8 +295,15 @@ def test_route_is_causal():
 
 
 # --------------------------------------------------------------------- O9 ---
+def fp32_logits(scores, scale):
+    """Attention logits as the method's arithmetic defines them: the exact
+    integer score q . k rounded to fp32 (exact below 2^24), times the fp32
+    scale, rounded to fp32."""
+    return (np.asarray(scores).astype(np.float32) * np.float32(scale)).astype(np.float64)
+
+
 def textbook_causal_attention(Q, K, V, scale):
-    s = (Q.astype(np.float64) @ K.astype(np.float64).T) * scale
+    s = fp32_logits(Q.astype(np.int64) @ K.astype(np.int64).T, scale)
     T = Q.shape[0]
     s[np.triu_indices(T, 1)] = -np.inf
     s -= s.max(axis=1, keepdims=True)
@@ -310,6 +339,33 @@ def test_attention_special_cases():
         np.testing.assert_array_equal(oracle.attend(j[:1], q, K, V, 0.25), V[j[0]])
 
 
+def test_attention_logits_are_rounded_to_fp32():
+    """Two keys with scores near 5 x 10^5 at scale fl32(1/sqrt(32)): the logits
+    are ~9 x 10^4, where an fp32 ulp is 2^-7, so rounding each logit to fp32
+    moves the two softmax weights measurably.  The output must equal the
+    two-key closed form with fp32 logits, sigma(a1 - a2) v1 + sigma(a2 - a1) v2,
+    and differ from the same form with exact logits (the case discriminates)."""
+    d = 32
+    scale = float(np.float32(1 / np.sqrt(d)))
+    q = np.full(d, 127, np.int8)
+    q[0] = 5
+    K = np.full((2, d), 127, np.int8)
+    K[1, 0] = 126                        # score 5 lower: logits ~0.9 apart
+    V = np.zeros((2, d), np.float32)
+    V[0], V[1] = 1.0, -1.0
+    s1 = int(K[0].astype(np.int64) @ q.astype(np.int64))
+    s2 = int(K[1].astype(np.int64) @ q.astype(np.int64))
+    a1 = float(np.float32(np.float32(s1) * np.float32(scale)))
+    a2 = float(np.float32(np.float32(s2) * np.float32(scale)))
+    e = np.exp(a2 - a1)
+    want = (1.0 - e) / (1.0 + e)
+    e64 = np.exp((s2 - s1) * scale)
+    exact = (1.0 - e64) / (1.0 + e64)
+    assert abs(want - exact) > 1e-4
+    out = oracle.attend(np.array([0, 1], np.int32), q, K, V, scale)
+    np.testing.assert_allclose(out, np.float32(want), rtol=0, atol=1e-7)
+
+
 def test_sparse_attention_equals_masked_dense_attention():
     torch = pytest.importorskip("torch")
     T, d = 256, 32
@@ -325,7 +381,12 @@ def test_sparse_attention_equals_masked_dense_attention():
         torch.from_numpy(Q.astype(np.float64))[None], torch.from_numpy(K.astype(np.float64))[None],
         torch.from_numpy(V.astype(np.float64))[None], attn_mask=torch.from_numpy(mask)[None],
         scale=scale)[0].numpy()
-    np.testing.assert_allclose(out["O"], ref, rtol=0, atol=1e-6)
+    # SDPA forms the logits in fp64; the oracle rounds each to fp32 (relative
+    # error <= 2^-24), which moves a softmax weight by at most a relative
+    # 2 * 2^-24 * max|a| and an output by that times 2 * max|v|
+    amax = float(np.abs(Q.astype(np.int64) @ K.astype(np.int64).T).max()) * scale
+    bound = 4 * 2.0 ** -24 * amax * float(np.abs(V).max()) + 1e-6
+    np.testing.assert_allclose(out["O"], ref, rtol=0, atol=bound)
 
 
 # -------------------------------------------------------------------- O10 ---
@@ -475,3 +536,134 @@ def test_split_is_linear_and_scale_exact_without_rounding():
     qr, kr = oracle.split_qk(X1[:, ::-1], W, heads, d, 0, 127, 127)
     np.testing.assert_array_equal(qr, q1[:, :, ::-1])
     np.testing.assert_array_equal(kr, k1[:, :, ::-1])
+
+
+# ------------------------------------------------- route load statistics ---
+# The per-query statistics (cover roots and expanded children, by level) are
+# the numerator of the byte model; these pins fix them by counting arguments
+# that do not run the beam.
+
+def stats_of(t, B, q, K, nodes, w, cap=96):
+    _, _, c, st = oracle.route(t, B, q, K, nodes, w, cap)
+    return c, st
+
+
+def check_stats_consistent(st):
+    assert st["cover_internal"] == sum(st["cover_by_level"][1:])
+    assert st["cover_leaf"] == st["cover_by_level"][0]
+    assert st["child_internal"] == sum(st["child_by_level"][1:])
+    assert st["child_leaf"] == st["child_by_level"][0]
+    assert all(v % 2 == 0 for v in st["child_by_level"]), "children come in pairs"
+
+
+def test_route_stats_cover_is_the_set_bits_of_the_domain():
+    """The cover roots of [0, m) are one node per set bit of m, at that bit's
+    level; no cover is formed when the window takes every key (r = 0)."""
+    T, d, w = 256, 8, 4
+    K, Q = rng_keys(61, T, d), rng_keys(62, T, d)
+    nodes = oracle.build_tree(K)
+    for B in (1, 4, 9, 40):
+        for t in range(T):
+            c, st = stats_of(t, B, Q[t], K, nodes, w)
+            n = min(w, c)
+            r = c - n
+            m = t + 1 - n
+            check_stats_consistent(st)
+            if r == 0:
+                assert st["cover_internal"] + st["cover_leaf"] == 0 and st["rounds"] == 0
+                continue
+            assert st["cover_internal"] + st["cover_leaf"] == bin(m).count("1")
+            assert st["cover_by_level"][:m.bit_length()] == [(m >> l) & 1 for l in range(m.bit_length())]
+
+
+def test_route_stats_dense_budget_expands_every_subtree():
+    """With a budget of every past key nothing is ever dropped, so every
+    internal node below a cover root is expanded: a root at level b yields
+    2^(b - l) children at each level l < b, and the rounds equal the highest
+    root level."""
+    T, d, w = 128, 8, 4
+    K, Q = rng_keys(63, T, d), rng_keys(64, T, d)
+    nodes = oracle.build_tree(K)
+    for t in range(T):
+        c, st = stats_of(t, T, Q[t], K, nodes, w, cap=T)
+        n = min(w, c)
+        m = t + 1 - n
+        if m == 0:
+            continue
+        roots = [l for l in range(m.bit_length()) if (m >> l) & 1]
+        want = [sum(1 << (b - l) for b in roots if b > l) for l in range(24)]
+        assert st["child_by_level"] == want
+        assert st["rounds"] == max(roots)
+
+
+def test_route_stats_wide_beam_closed_form():
+    """Domain [0, 2^h) with r >= 2^(h-1): every round keeps all candidates
+    until the leaves, so round k yields 2^k children at level h - k."""
+    T, d, w = 128, 8, 4
+    r_ = np.random.default_rng(65)
+    K = r_.integers(-3, 4, size=(T, d)).astype(np.int8)
+    q = r_.integers(-3, 4, size=d).astype(np.int8)
+    nodes = oracle.build_tree(K)
+    for h in range(1, 7):
+        m = 1 << h
+        t = m - 1 + w
+        for rr in sorted({max(1, m // 2), m}):
+            c, st = stats_of(t, rr + w, q, K, nodes, w, cap=128)
+            assert st["child_by_level"][:h] == [1 << (h - l) for l in range(h)]
+            assert not any(st["child_by_level"][h:])
+            assert st["rounds"] == h
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_route_stats_width_one_follows_a_single_path(seed):
+    """r = 1: one beam node; each round expands it into two children, from the
+    level of the best cover root down to the leaves."""
+    T, d, w = 256, 16, 4
+    K, Q = rng_keys(500 + seed, T, d, -8, 8), rng_keys(600 + seed, T, d, -9, 9)
+    P = np.zeros((T + 1, d), np.int64)
+    P[1:] = np.cumsum(K.astype(np.int64), axis=0)
+    nodes = oracle.build_tree(K)
+    for t in range(w, T):
+        c, st = stats_of(t, w + 1, Q[t], K, nodes, w)
+        m = t + 1 - w
+        # the best cover root, from brute-force prefix sums (as greedy_r1)
+        roots = cover(m)
+        sc = lambda lv, a: int((P[a + (1 << lv)] - P[a]) @ Q[t].astype(np.int64))
+        lv, _ = min(roots, key=lambda x: (-sc(*x), x[1]))
+        assert st["child_by_level"] == [2 if l < lv else 0 for l in range(24)]
+        assert st["rounds"] == lv
+
+
+def test_route_stats_zero_query_leftmost_refinement():
+    """q = 0: every score ties, so each round keeps the r leftmost candidates.
+    The beam before round k is then the r leftmost nodes of the cover refined
+    k-1 times (each root of level b split into its sub-trees of level
+    max(b - k + 1, 0)); round k expands its internal nodes."""
+    T, d, w = 128, 8, 4
+    K = rng_keys(66, T, d)
+    q = np.zeros(d, np.int8)
+    nodes = oracle.build_tree(K)
+    for B in (6, 13, 30):
+        for t in range(T):
+            c, st = stats_of(t, B, q, K, nodes, w)
+            n = min(w, c)
+            r = c - n
+            m = t + 1 - n
+            if r == 0:
+                continue
+            want = [0] * 24
+            rounds = 0
+            for k in range(1, 25):
+                refined = []
+                for lv, a in cover(m):   # ascending start order
+                    lk = max(lv - (k - 1), 0)
+                    refined += [(lk, a + i * (1 << lk)) for i in range(1 << (lv - lk))]
+                beam = refined[:r]
+                internal = [lv for lv, _ in beam if lv > 0]
+                if not internal:
+                    break
+                rounds += 1
+                for lv in internal:
+                    want[lv - 1] += 2
+            assert st["child_by_level"] == want
+            assert st["rounds"] == rounds
