@@ -19,10 +19,13 @@
  * --------------------------------
  * Pointers.  Every array argument is DEVICE memory owned by the caller; the
  * library never allocates or frees device memory, and keeps no state between
- * calls.  Scratch space is passed explicitly as (ws, ws_bytes), sized by
- * alhr_workspace_bytes().  Array base pointers must be 16-byte aligned.
- * `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
- * are asynchronous: results are valid once the caller synchronises `stream`.
+ * calls.  Scratch space is passed explicitly as (ws, ws_bytes), at least
+ * alhr_workspace_bytes() bytes; its contents need no initialisation and are
+ * not meaningful between calls, and two calls that may run at the same time
+ * (different streams) must not share one.  Array base pointers must be
+ * 16-byte aligned.  `stream` is a hipStream_t passed as void* (NULL = the
+ * null stream).  Calls are asynchronous: results are valid once the caller
+ * synchronises `stream`.
  *
  * Layouts (row-major, d contiguous; P = batch * heads pairs):
  *   Q, K   int8  [batch, heads, T, d]     queries / keys
@@ -109,8 +112,9 @@ typedef struct alhr_config {
  * cfg is invalid. */
 int32_t alhr_tree_int16_levels(const alhr_config *cfg);
 
-/* Bytes of scratch that alhr_predict_budget / alhr_prepare / alhr_forward
- * need (a multiple of 256; 0 if cfg is invalid). */
+/* Bytes of scratch (ws) that alhr_predict_budget / alhr_prepare /
+ * alhr_forward need: the predictor's per-chunk class totals (a multiple of
+ * 256; 0 if cfg is invalid). */
 size_t alhr_workspace_bytes(const alhr_config *cfg);
 
 /* Tree of key sums (README, opening paragraph and "Inference stage": one
@@ -140,23 +144,25 @@ alhr_status alhr_prepare(const alhr_config *cfg, const int8_t *Q,
                          void *stream);
 
 /* Routing (README "Inference stage" and "Training stage"): for each query t
- * with budget B_t (budget[t], or fixed_budget when budget is NULL; values
- * must lie in [1, max_budget]): C_t = min(B_t, t+1) keys; the n_t =
- * min(window, C_t) keys t, t-1, ...; then a beam of width r_t = C_t - n_t
- * descends from the maximal complete subtrees covering [0, t+1-n_t),
- * expanding every internal beam node each round and keeping the r_t best
- * nodes by (q . node_sum descending, first position ascending).  Writes idx
- * and count. */
+ * with budget B_t (budget[t], or fixed_budget when budget is NULL; array
+ * values outside [1, max_budget] are clamped into it): C_t = min(B_t, t+1)
+ * keys; the n_t = min(window, C_t) keys t, t-1, ...; then a beam of width
+ * r_t = C_t - n_t descends from the maximal complete subtrees covering
+ * [0, t+1-n_t), expanding every internal beam node each round and keeping
+ * the r_t best nodes by (q . node_sum descending, first position ascending).
+ * Writes idx and count; score (nullable) int32 [batch, heads, T, max_budget]
+ * receives q . K[j] for each selected j in idx order and 0 in the padding. */
 alhr_status alhr_route(const alhr_config *cfg, const int8_t *Q,
                        const int8_t *K, const int32_t *nodes,
                        const int32_t *budget, int32_t fixed_budget,
-                       int32_t *idx, int32_t *count, void *stream);
+                       int32_t *idx, int32_t *count, int32_t *score,
+                       void *stream);
 
-/* Per-query load counts of the routing step, for byte accounting: stats is
- * int32 [batch, heads, T, 4] = (int32 tree rows loaded, int16 tree rows
- * loaded, key rows loaded by the descent, selected keys C); the neighbour
- * key rows are min(window, C).  Same arguments as alhr_route; idx and count
- * are written as by alhr_route. */
+/* Per-query load counts of the routing step (README "Inference stage"), for
+ * byte accounting: stats is int32 [batch, heads, T, 4] = (int32 tree rows
+ * loaded, int16 tree rows loaded, key rows loaded by the descent, selected
+ * keys C); the neighbour key rows are min(window, C).  Arguments as for
+ * alhr_route without score; idx and count are written as by alhr_route. */
 alhr_status alhr_route_stats(const alhr_config *cfg, const int8_t *Q,
                              const int8_t *K, const int32_t *nodes,
                              const int32_t *budget, int32_t fixed_budget,
@@ -164,26 +170,31 @@ alhr_status alhr_route_stats(const alhr_config *cfg, const int8_t *Q,
                              void *stream);
 
 /* Sparse attention over selected keys (README "Inference stage"): for each
- * query, a_j = scale * (Q[t] . K[j]) over j in idx[t][0..count[t]), and
- * O[t] = sum_j softmax(a)_j V[j], in fp32. */
+ * query, a_j = fl32(fl32(Q[t] . K[j]) * scale) over j in idx[t][0..count[t]),
+ * and O[t] = sum_j softmax(a)_j V[j], in fp32.  count values are clamped to
+ * [0, max_budget]; positions outside [0, T) are left out of the softmax; a
+ * query with no valid position gets O[t] = 0. */
 alhr_status alhr_sparse_attend(const alhr_config *cfg, const int8_t *Q,
                                const int8_t *K, const float *V,
                                const int32_t *idx, const int32_t *count,
                                float *O, void *stream);
 
-/* Fused routing + attention in one pass per query (same results as
- * alhr_route followed by alhr_sparse_attend; the leaf scores found by the
- * descent are reused as logits). */
+/* Fused routing + attention in one pass per query (README "Inference
+ * stage": the descent's keys, then attention over them; the openai-hub
+ * article, section "判断：方向对，但离“大模型可用”还有两道关", on dedicated
+ * kernels and batched routing).  Same results as alhr_route followed by
+ * alhr_sparse_attend; the leaf scores found by the descent are reused as
+ * logits. */
 alhr_status alhr_route_attend(const alhr_config *cfg, const int8_t *Q,
                               const int8_t *K, const float *V,
                               const int32_t *nodes, const int32_t *budget,
                               int32_t fixed_budget, int32_t *idx,
                               int32_t *count, float *O, void *stream);
 
-/* The whole prefill path: build the tree, predict budgets (W != NULL; else
- * every query uses fixed_budget), route and attend.  budget (nullable)
- * receives the predicted budgets.  ws as for alhr_predict_budget (unused
- * when W is NULL). */
+/* The whole prefill path of the README's "Inference stage": build the tree,
+ * predict budgets (W != NULL; else every query uses fixed_budget), route and
+ * attend.  budget (nullable) receives the predicted budgets.  ws as for
+ * alhr_predict_budget (unused when W is NULL). */
 alhr_status alhr_forward(const alhr_config *cfg, const int8_t *Q,
                          const int8_t *K, const float *V, const int8_t *W,
                          int32_t fixed_budget, int32_t *nodes,
@@ -209,9 +220,11 @@ alhr_status alhr_append(const alhr_config *cfg, int32_t pos,
                         float *V, int32_t *nodes, int32_t *prefix,
                         void *stream);
 
-/* Decode step: route and attend the single query q_new (int8 [batch, heads,
- * d]) at position pos of every pair, after alhr_append(pos).  The budget
- * comes from W and prefix (= S[pos]) when W != NULL, else fixed_budget.
+/* Decode step (openai-hub article, section "ALHR是什么": one new token at a
+ * time, routed through the cached tree; README "Inference stage" for the
+ * steps): route and attend the single query q_new (int8 [batch, heads, d])
+ * at position pos of every pair, after alhr_append(pos).  The budget comes
+ * from W and prefix (= S[pos]) when W != NULL, else fixed_budget.
  * Outputs are per pair: budget (nullable) int32 [batch, heads], idx int32
  * [batch, heads, max_budget], count int32 [batch, heads], O fp32 [batch,
  * heads, d]. */

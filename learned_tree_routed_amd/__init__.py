@@ -137,7 +137,7 @@ def load():
         "alhr_build_tree": ([cfgp, P, P, P], C.c_int),
         "alhr_predict_budget": ([cfgp, P, P, P, P, P, sz, P], C.c_int),
         "alhr_prepare": ([cfgp, P, P, P, P, P, P, sz, P], C.c_int),
-        "alhr_route": ([cfgp, P, P, P, P, i32, P, P, P], C.c_int),
+        "alhr_route": ([cfgp, P, P, P, P, i32, P, P, P, P], C.c_int),
         "alhr_route_stats": ([cfgp, P, P, P, P, i32, P, P, P, P], C.c_int),
         "alhr_sparse_attend": ([cfgp, P, P, P, P, P, P, P], C.c_int),
         "alhr_route_attend": ([cfgp, P, P, P, P, P, i32, P, P, P, P], C.c_int),
@@ -297,11 +297,18 @@ def _route_args(cfg, Q, K, nodes, budget, idx, count):
     return idx, count
 
 
-def alhr_route(cfg, Q, K, nodes, budget=None, fixed_budget=0, idx=None, count=None, stream=None):
+def alhr_route(cfg, Q, K, nodes, budget=None, fixed_budget=0, idx=None, count=None,
+               score=None, with_score=False, stream=None):
+    """Routing only.  Returns (idx, count), or (idx, count, score) when a score
+    tensor is passed or with_score is set (q . K[j] of the selected keys, 0 in
+    the padding)."""
+    torch = _torch()
     idx, count = _route_args(cfg, Q, K, nodes, budget, idx, count)
+    if score is not None or with_score:
+        score = _out(score, "score", torch.int32, _shapes(cfg)[2], Q.device)
     _call("alhr_route", C.byref(cfg.c()), _ptr(Q), _ptr(K), _ptr(nodes), _ptr(budget),
-          int(fixed_budget), _ptr(idx), _ptr(count), _stream(stream))
-    return idx, count
+          int(fixed_budget), _ptr(idx), _ptr(count), _ptr(score), _stream(stream))
+    return (idx, count) if score is None else (idx, count, score)
 
 
 def alhr_route_stats(cfg, Q, K, nodes, budget=None, fixed_budget=0, idx=None, count=None,
@@ -352,14 +359,15 @@ def alhr_forward(cfg, Q, K, V, W=None, fixed_budget=0, nodes=None, budget=None, 
     idx = _out(idx, "idx", torch.int32, idx_shape, Q.device)
     count = _out(count, "count", torch.int32, per_q, Q.device)
     O = _out(O, "O", torch.float32, rows, Q.device)
-    nbytes = 0
     if W is not None:
         _check("W", W, torch.int8, (cfg.n_classes, 2 * cfg.d), Q.device)
         budget = _out(budget, "budget", torch.int32, per_q, Q.device)
         ws, nbytes = _workspace(cfg, ws, Q.device)
+    else:
+        ws, nbytes = None, 0
     _call("alhr_forward", C.byref(cfg.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(W),
           int(fixed_budget), _ptr(nodes), _ptr(budget), _ptr(idx), _ptr(count), _ptr(O),
-          _ptr(ws) if W is not None else None, nbytes, _stream(stream))
+          _ptr(ws), nbytes, _stream(stream))
     return {"nodes": nodes, "budget": budget, "idx": idx, "count": count, "O": O}
 
 

@@ -125,6 +125,17 @@ alhr_status device_status(const char* fn, hipError_t e)
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+size_t workspace_bytes(const alhr::Shape& s) { return alhr::predict_ws_bytes(s); }
+
+alhr_status check_ws(const char* fn, const alhr::Shape& s, const void* ws, size_t ws_bytes)
+{
+    const size_t need = workspace_bytes(s);
+    if (!ws || ws_bytes < need || !aligned16(ws))
+        return fail(ALHR_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu%s%s)", fn,
+                    need, ws_bytes, ws ? "" : ", NULL", ws && !aligned16(ws) ? ", misaligned" : "");
+    return ALHR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -157,7 +168,7 @@ size_t alhr_workspace_bytes(const alhr_config* cfg)
 {
     alhr::Shape s;
     if (check_config("alhr_workspace_bytes", cfg, &s) != ALHR_OK) return 0;
-    return alhr::predict_ws_bytes(s);
+    return workspace_bytes(s);
 }
 
 alhr_status alhr_build_tree(const alhr_config* cfg, const int8_t* K, int32_t* nodes,
@@ -183,12 +194,10 @@ alhr_status alhr_predict_budget(const alhr_config* cfg, const int8_t* Q, const i
     ALHR_NEED_PTR(K);
     ALHR_NEED_PTR(W);
     ALHR_NEED_PTR(budget);
-    const size_t need = alhr::predict_ws_bytes(s);
-    if (!ws || ws_bytes < need || !aligned16(ws))
-        return fail(ALHR_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu%s)", fn, need,
-                    ws_bytes, ws ? "" : ", NULL");
+    if (alhr_status st = check_ws(fn, s, ws, ws_bytes)) return st;
     (void)hipGetLastError();
-    return device_status(fn, alhr::launch_predict(s, Q, K, W, budget, ws, as_stream(stream)));
+    return device_status(fn, alhr::launch_predict(s, Q, K, W, budget, ws,
+                                                  as_stream(stream)));
 }
 
 alhr_status alhr_prepare(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
@@ -204,10 +213,7 @@ alhr_status alhr_prepare(const alhr_config* cfg, const int8_t* Q, const int8_t* 
         ALHR_NEED_PTR(Q);
         ALHR_NEED_PTR(W);
         ALHR_NEED_PTR(budget);
-        const size_t need = alhr::predict_ws_bytes(s);
-        if (!ws || ws_bytes < need || !aligned16(ws))
-            return fail(ALHR_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu%s)", fn,
-                        need, ws_bytes, ws ? "" : ", NULL");
+        if (alhr_status st = check_ws(fn, s, ws, ws_bytes)) return st;
     }
     (void)hipGetLastError();
     hipStream_t st = as_stream(stream);
@@ -218,8 +224,8 @@ alhr_status alhr_prepare(const alhr_config* cfg, const int8_t* Q, const int8_t* 
 static alhr_status route_common(const char* fn, const alhr_config* cfg, const int8_t* Q,
                                 const int8_t* K, const float* V, const int32_t* nodes,
                                 const int32_t* budget, int32_t fixed_budget, int32_t* idx,
-                                int32_t* count, float* O, int32_t* stats, bool attend,
-                                void* stream)
+                                int32_t* count, float* O, int32_t* stats, int32_t* score,
+                                bool attend, void* stream)
 {
     alhr::Shape s;
     if (alhr_status st = check_config(fn, cfg, &s)) return st;
@@ -233,18 +239,20 @@ static alhr_status route_common(const char* fn, const alhr_config* cfg, const in
         ALHR_NEED_PTR(O);
     }
     if (alhr_status st = check_fixed(fn, cfg, budget, fixed_budget)) return st;
+    if (score && !aligned16(score))
+        return fail(ALHR_ERR_ARG, "%s: argument 'score' is not 16-byte aligned", fn);
     (void)hipGetLastError();
     return device_status(fn, alhr::launch_route(s, Q, K, attend ? V : nullptr, nodes, budget,
                                                 fixed_budget, idx, count, attend ? O : nullptr,
-                                                stats, as_stream(stream)));
+                                                stats, score, as_stream(stream)));
 }
 
 alhr_status alhr_route(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
                        const int32_t* nodes, const int32_t* budget, int32_t fixed_budget,
-                       int32_t* idx, int32_t* count, void* stream)
+                       int32_t* idx, int32_t* count, int32_t* score, void* stream)
 {
     return route_common("alhr_route", cfg, Q, K, nullptr, nodes, budget, fixed_budget, idx,
-                        count, nullptr, nullptr, false, stream);
+                        count, nullptr, nullptr, score, false, stream);
 }
 
 alhr_status alhr_route_stats(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
@@ -254,7 +262,7 @@ alhr_status alhr_route_stats(const alhr_config* cfg, const int8_t* Q, const int8
     const char* fn = "alhr_route_stats";
     ALHR_NEED_PTR(stats);
     return route_common(fn, cfg, Q, K, nullptr, nodes, budget, fixed_budget, idx, count,
-                        nullptr, stats, false, stream);
+                        nullptr, stats, nullptr, false, stream);
 }
 
 alhr_status alhr_sparse_attend(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
@@ -280,7 +288,7 @@ alhr_status alhr_route_attend(const alhr_config* cfg, const int8_t* Q, const int
                               void* stream)
 {
     return route_common("alhr_route_attend", cfg, Q, K, V, nodes, budget, fixed_budget, idx,
-                        count, O, nullptr, true, stream);
+                        count, O, nullptr, nullptr, true, stream);
 }
 
 alhr_status alhr_forward(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
@@ -305,10 +313,7 @@ alhr_status alhr_forward(const alhr_config* cfg, const int8_t* Q, const int8_t* 
                                       "predicted budgets)", fn);
         if (!aligned16(budget))
             return fail(ALHR_ERR_ARG, "%s: argument 'budget' is not 16-byte aligned", fn);
-        const size_t need = alhr::predict_ws_bytes(s);
-        if (!ws || ws_bytes < need || !aligned16(ws))
-            return fail(ALHR_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu%s)", fn,
-                        need, ws_bytes, ws ? "" : ", NULL");
+        if (alhr_status st = check_ws(fn, s, ws, ws_bytes)) return st;
     } else if (fixed_budget < 1 || fixed_budget > cfg->max_budget) {
         return fail(ALHR_ERR_ARG, "%s: fixed_budget = %d must be in [1, max_budget = %d]", fn,
                     fixed_budget, cfg->max_budget);
@@ -320,7 +325,7 @@ alhr_status alhr_forward(const alhr_config* cfg, const int8_t* Q, const int8_t* 
                      : alhr::launch_build(s, K, nodes, st);
     if (e == hipSuccess)
         e = alhr::launch_route(s, Q, K, V, nodes, W ? budget : nullptr, fixed_budget, idx, count,
-                               O, nullptr, st);
+                               O, nullptr, nullptr, st);
     return device_status(fn, e);
 }
 

@@ -9,7 +9,16 @@ namespace alhr {
 constexpr int kWave = 64;
 constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, round-robin dispatch
 
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
+// The lane index, opaque to the optimiser: values derived from it are
+// recomputed where they are used instead of being hoisted out of loops and
+// held in vector registers for a kernel's whole run (which cost the
+// persistent routing kernel two waves per SIMD).
+__device__ __forceinline__ int lane_id()
+{
+    int l = __lane_id();
+    asm volatile("" : "+v"(l));
+    return l;
+}
 
 // Keep the compiler from moving LDS accesses across this point; LDS traffic
 // of one wave is processed in order by the hardware.

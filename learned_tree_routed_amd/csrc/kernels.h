@@ -36,10 +36,12 @@ hipError_t launch_prep(const Shape& s, const int8_t* Q, const int8_t* K, const i
 hipError_t launch_predict(const Shape& s, const int8_t* Q, const int8_t* K, const int8_t* W,
                           int32_t* budget, void* ws, hipStream_t st);
 
-// O == nullptr: routing only; stats != nullptr: also write per-query load counts.
+// O == nullptr: routing only (score, if not null, receives q . K[j] of the
+// selected keys); stats != nullptr: write per-query load counts instead.
 hipError_t launch_route(const Shape& s, const int8_t* Q, const int8_t* K, const float* V,
                         const int32_t* nodes, const int32_t* budget, int fixed_budget,
-                        int32_t* idx, int32_t* count, float* O, int32_t* stats, hipStream_t st);
+                        int32_t* idx, int32_t* count, float* O, int32_t* stats, int32_t* score,
+                        hipStream_t st);
 
 hipError_t launch_attend(const Shape& s, const int8_t* Q, const int8_t* K, const float* V,
                          const int32_t* idx, const int32_t* count, float* O, hipStream_t st);

@@ -571,13 +571,21 @@ __device__ __forceinline__ void write_selection(const WaveLds& sm, int C, int ma
     if (lane == 0) *count_out = C;
 }
 
-// softmax over sm.score[0, C) * scale and the weighted sum of value rows.
+// q . K[j] of the selected keys in idx order, 0 in the padding.
+__device__ __forceinline__ void write_scores(const WaveLds& sm, int C, int max_budget,
+                                             int32_t* __restrict__ score_row)
+{
+    for (int c = lane_id(); c < max_budget; c += kWave) score_row[c] = c < C ? sm.score[c] : 0;
+}
+
+// softmax over sm.score[0, C) * scale and the weighted sum of value rows,
+// returned per lane (see store_output).
 // Positions outside [0, T) (possible only in caller-supplied index sets,
 // CHECK = true) are left out of the softmax and never loaded; with none left
 // the output is 0.  Routed sets (CHECK = false) hold valid positions only.
 template <int D, bool CHECK>
-__device__ void attend_selected(WaveLds& sm, int C, int T, float scale,
-                                const float* __restrict__ values_pair, float* __restrict__ out)
+__device__ float4 attend_selected(WaveLds& sm, int C, int T, float scale,
+                                  const float* __restrict__ values_pair)
 {
     constexpr int LPV = D / 4, RPV = kWave / LPV;
     const int lane = lane_id();
@@ -655,50 +663,93 @@ __device__ void attend_selected(WaveLds& sm, int C, int T, float scale,
         acc.z += __shfl_xor(acc.z, o);
         acc.w += __shfl_xor(acc.w, o);
     }
-    if (rv == 0) {
-        const float inv = z > 0.0f ? 1.0f / z : 0.0f;
-        reinterpret_cast<float4*>(out)[cv] =
-            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    }
+    const float inv = z > 0.0f ? 1.0f / z : 0.0f;
+    return make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
+// Every lane holds the output columns 4 (lane % (d/4)) .. + 3 after
+// attend_selected; the first d/4 lanes store the row.
+template <int D>
+__device__ __forceinline__ void store_output(float* __restrict__ out, float4 o)
+{
+    const int lane = lane_id();
+    if (lane < D / 4) reinterpret_cast<float4*>(out)[lane] = o;
 }
 
 // ---- prefill: one wave per (pair, t), expensive (late) queries first -----
+struct RouteArgs {
+    const int8_t* Q;
+    const int8_t* K;
+    const float* V;
+    const int32_t* nodes;
+    const int32_t* budget;   // nullable: fixed_budget for every query
+    int32_t* idx;
+    int32_t* count;
+    float* O;                // ATTEND
+    int32_t* stats;          // STATS
+    int32_t* score;          // nullable, routing without attention only
+    int fixed_budget, P, T, L, l16, window, max_budget;
+    int interleave;          // see k_route
+    float scale;
+    uint64_t q0, nq;         // the launch covers queries [q0, q0 + nq)
+};
+
+// Query gw of the launch order is pair gw >> L at position T-1 - (gw mod T):
+// pair-major, and within a pair from t = T-1 down (the late queries, whose
+// covers are deepest, start first).
 template <int D, bool MUL24, bool ATTEND, bool STATS>
-__global__ __launch_bounds__(kThreads) void k_route(
-    const int8_t* __restrict__ Q, const int8_t* __restrict__ K, const float* __restrict__ V,
-    const int32_t* __restrict__ nodes, const int32_t* __restrict__ budget, int fixed_budget,
-    int32_t* __restrict__ idx, int32_t* __restrict__ count, float* __restrict__ O,
-    int32_t* __restrict__ stats, int P, int T, int L, int l16, int window, int max_budget,
-    float scale, uint64_t q0, uint64_t nq)
+__device__ __forceinline__ void route_one(const RouteArgs& a, uint64_t gw, WaveLds& sm)
+{
+    const int T = a.T;
+    const uint32_t pair = uniform((uint32_t)(gw >> a.L));
+    const int t = uniform(T - 1 - (int)((uint32_t)gw & (uint32_t)(T - 1)));
+    const size_t qrow = (size_t)pair * T + t;
+    QueryRegs<D> q;
+    load_query<D>(a.Q + qrow * D, lane_id() % (D / 16), q);
+    // budgets outside [1, max_budget] are clamped: the beam and idx rows hold max_budget
+    int B = uniform(a.budget ? a.budget[qrow] : a.fixed_budget);
+    B = B < 1 ? 1 : (B > a.max_budget ? a.max_budget : B);
+    RouteCounts cnt{0, 0, 0};
+    const int C = route_query<D, MUL24, STATS>(a.nodes + (size_t)pair * T * D,
+                                                a.K + (size_t)pair * T * D, T, a.L, a.l16, t, B,
+                                                a.window, q, sm, cnt);
+    write_selection(sm, C, a.max_budget, a.idx + qrow * a.max_budget, a.count + qrow);
+    if (STATS && lane_id() == 0) {
+        a.stats[qrow * 4 + 0] = cnt.tree_rows;
+        a.stats[qrow * 4 + 1] = cnt.tree16_rows;
+        a.stats[qrow * 4 + 2] = cnt.key_rows;
+        a.stats[qrow * 4 + 3] = C;
+    }
+    if constexpr (!ATTEND && !STATS) {
+        if (a.score) write_scores(sm, C, a.max_budget, a.score + qrow * a.max_budget);
+    }
+    if constexpr (ATTEND)
+        store_output<D>(a.O + qrow * D,
+                        attend_selected<D, false>(sm, C, T, a.scale, a.V + (size_t)pair * T * D));
+}
+
+// Which queries each XCD runs (workgroups are dealt round-robin to the 8 XCDs,
+// each with its own L2).  With at least kPairsPerXcd pairs per XCD, every XCD
+// takes one contiguous range of queries, i.e. whole pairs, whose rows then stay
+// in its L2; the budgets of the pairs in a range average out.  With fewer,
+// the pairs' budgets (nearly constant within a pair for a predictor dominated
+// by the key sum, and different between pairs) would leave the XCDs unequally
+// loaded - the launch lasts as long as its busiest XCD - so consecutive
+// workgroups go to consecutive XCDs instead: every XCD takes an equal share of
+// every pair, at the price of each L2 holding every pair's rows in turn (the
+// openai-hub article, section "次二次复杂度成立，需要满足三个前提", on GPU
+// utilisation under divergent tree search).
+constexpr int kPairsPerXcd = 8;
+
+template <int D, bool MUL24, bool ATTEND, bool STATS>
+__global__ __launch_bounds__(kThreads) void k_route(const RouteArgs a)
 {
     __shared__ WaveLds smem[kWavesPerBlock];
     const int wid = uniform((int)(threadIdx.x / kWave));
-    const uint64_t lw = (uint64_t)xcd_logical_block() * kWavesPerBlock + wid;
-    if (lw >= nq) return;
-    const uint64_t gw = q0 + lw;   // query index over all P * T (launches cover ranges)
-    const int pair = uniform((int)(gw / (uint64_t)T));
-    const int t = uniform(T - 1 - (int)(gw % (uint64_t)T));
-    const size_t qrow = (size_t)pair * T + t;
-    const int s = lane_id() % (D / 16);
-    QueryRegs<D> q;
-    load_query<D>(Q + qrow * D, s, q);
-    // budgets outside [1, max_budget] are clamped: the beam and idx rows hold max_budget
-    int B = uniform(budget ? budget[qrow] : fixed_budget);
-    B = B < 1 ? 1 : (B > max_budget ? max_budget : B);
-    WaveLds& sm = smem[wid];
-    RouteCounts cnt{0, 0, 0};
-    const int C = route_query<D, MUL24, STATS>(nodes + (size_t)pair * T * D,
-                                                K + (size_t)pair * T * D, T, L, l16, t, B,
-                                                window, q, sm, cnt);
-    write_selection(sm, C, max_budget, idx + qrow * max_budget, count + qrow);
-    if (STATS && lane_id() == 0) {
-        stats[qrow * 4 + 0] = cnt.tree_rows;
-        stats[qrow * 4 + 1] = cnt.tree16_rows;
-        stats[qrow * 4 + 2] = cnt.key_rows;
-        stats[qrow * 4 + 3] = C;
-    }
-    if constexpr (ATTEND)
-        attend_selected<D, false>(sm, C, T, scale, V + (size_t)pair * T * D, O + qrow * D);
+    const uint64_t blk = a.interleave ? blockIdx.x : xcd_logical_block();
+    const uint64_t lw = blk * kWavesPerBlock + wid;
+    if (lw >= a.nq) return;
+    route_one<D, MUL24, ATTEND, STATS>(a, a.q0 + lw, smem[wid]);
 }
 
 // ---- attention over given index sets -------------------------------------
@@ -741,7 +792,7 @@ __global__ __launch_bounds__(kThreads) void k_attend(const int8_t* __restrict__ 
         }
     }
     wave_sync();
-    attend_selected<D, true>(sm, C, T, scale, V + (size_t)pair * T * D, O + qrow * D);
+    store_output<D>(O + qrow * D, attend_selected<D, true>(sm, C, T, scale, V + (size_t)pair * T * D));
 }
 
 // ---- decode: one wave per pair, query at position pos --------------------
@@ -1013,28 +1064,30 @@ unsigned grid_for_waves(uint64_t waves)
     return (unsigned)blocks;
 }
 
+template <int D, bool MUL24, bool ATTEND, bool STATS>
+hipError_t launch_one(const RouteArgs& a, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_route<D, MUL24, ATTEND, STATS>), dim3(grid_for_waves(a.nq)),
+                       dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
 template <int D, bool MUL24>
 hipError_t route_d(const Shape& s, const int8_t* Q, const int8_t* K, const float* V,
                    const int32_t* nodes, const int32_t* budget, int fixed_budget, int32_t* idx,
-                   int32_t* count, float* O, int32_t* stats, hipStream_t st)
+                   int32_t* count, float* O, int32_t* stats, int32_t* score, hipStream_t st)
 {
+    RouteArgs a{Q, K, V, nodes, budget, idx, count, O, stats, score, fixed_budget, s.P, s.T,
+                s.L, s.l16, s.window, s.max_budget, 0, s.scale, 0, 0};
     const uint64_t total = (uint64_t)s.P * s.T;
     for (uint64_t q0 = 0; q0 < total; q0 += kQueriesPerLaunch) {
-        const uint64_t nq = total - q0 < kQueriesPerLaunch ? total - q0 : kQueriesPerLaunch;
-        const dim3 grid(grid_for_waves(nq));
-        if (stats)
-            hipLaunchKernelGGL((k_route<D, MUL24, false, true>), grid, dim3(kThreads), 0, st, Q, K,
-                               V, nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T,
-                               s.L, s.l16, s.window, s.max_budget, s.scale, q0, nq);
-        else if (O)
-            hipLaunchKernelGGL((k_route<D, MUL24, true, false>), grid, dim3(kThreads), 0, st, Q, K,
-                               V, nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T,
-                               s.L, s.l16, s.window, s.max_budget, s.scale, q0, nq);
-        else
-            hipLaunchKernelGGL((k_route<D, MUL24, false, false>), grid, dim3(kThreads), 0, st, Q,
-                               K, V, nodes, budget, fixed_budget, idx, count, O, stats, s.P, s.T,
-                               s.L, s.l16, s.window, s.max_budget, s.scale, q0, nq);
-        const hipError_t e = hipGetLastError();
+        a.q0 = q0;
+        a.nq = total - q0 < kQueriesPerLaunch ? total - q0 : kQueriesPerLaunch;
+        a.interleave = a.nq < (uint64_t)kXcds * kPairsPerXcd * s.T;
+        hipError_t e;
+        if (stats) e = launch_one<D, MUL24, false, true>(a, st);
+        else if (O) e = launch_one<D, MUL24, true, false>(a, st);
+        else e = launch_one<D, MUL24, false, false>(a, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -1043,12 +1096,13 @@ hipError_t route_d(const Shape& s, const int8_t* Q, const int8_t* K, const float
 template <int D>
 hipError_t route_dispatch(const Shape& s, const int8_t* Q, const int8_t* K, const float* V,
                           const int32_t* nodes, const int32_t* budget, int fixed_budget,
-                          int32_t* idx, int32_t* count, float* O, int32_t* stats, hipStream_t st)
+                          int32_t* idx, int32_t* count, float* O, int32_t* stats, int32_t* score,
+                          hipStream_t st)
 {
     return s.mul24 ? route_d<D, true>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O,
-                                      stats, st)
+                                      stats, score, st)
                    : route_d<D, false>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O,
-                                       stats, st);
+                                       stats, score, st);
 }
 
 template <int D>
@@ -1079,16 +1133,21 @@ hipError_t decode_d(const Shape& s, int pos, const int8_t* q_new, const int8_t* 
 
 hipError_t launch_route(const Shape& s, const int8_t* Q, const int8_t* K, const float* V,
                         const int32_t* nodes, const int32_t* budget, int fixed_budget,
-                        int32_t* idx, int32_t* count, float* O, int32_t* stats, hipStream_t st)
+                        int32_t* idx, int32_t* count, float* O, int32_t* stats, int32_t* score,
+                        hipStream_t st)
 {
+#define ALHR_RD(DD)                                                                              \
+    return route_dispatch<DD>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O, stats,    \
+                              score, st)
     switch (s.d) {
-        case 16: return route_dispatch<16>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O, stats, st);
-        case 32: return route_dispatch<32>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O, stats, st);
-        case 64: return route_dispatch<64>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O, stats, st);
-        case 128: return route_dispatch<128>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O, stats, st);
-        case 256: return route_dispatch<256>(s, Q, K, V, nodes, budget, fixed_budget, idx, count, O, stats, st);
+        case 16: ALHR_RD(16);
+        case 32: ALHR_RD(32);
+        case 64: ALHR_RD(64);
+        case 128: ALHR_RD(128);
+        case 256: ALHR_RD(256);
         default: return hipErrorInvalidValue;
     }
+#undef ALHR_RD
 }
 
 hipError_t launch_attend(const Shape& s, const int8_t* Q, const int8_t* K, const float* V,

@@ -76,10 +76,10 @@ def status(fn, *args):
 
 
 def route_call(c, **over):
-    a = dict(Q=P0, K=P0, nodes=P0, budget=NULL, fixed=16, idx=P0, count=P0)
+    a = dict(Q=P0, K=P0, nodes=P0, budget=NULL, fixed=16, idx=P0, count=P0, score=NULL)
     a.update(over)
     return status("alhr_route", C.byref(c.c()), a["Q"], a["K"], a["nodes"], a["budget"],
-                  a["fixed"], a["idx"], a["count"], NULL)
+                  a["fixed"], a["idx"], a["count"], a["score"], NULL)
 
 
 @pytestmark_cpu
@@ -152,6 +152,21 @@ def test_workspace_checks():
                           NULL)
     assert st == -1
     assert alhr.alhr_workspace_bytes(cfg(T=3)) == 0
+
+
+@pytestmark_cpu
+def test_route_score_output_checks():
+    """alhr_route takes an optional score output, which must be aligned when
+    given; alhr_forward without W needs no workspace."""
+    c = cfg()
+    st, msg = route_call(c, score=P_ODD)
+    assert st == -1 and "'score'" in msg
+    # valid with or without a score output: reaches the device
+    assert route_call(c, score=P0)[0] == -3
+    assert route_call(c)[0] == -3
+    lib = alhr.load()
+    cc = C.byref(c.c())
+    assert lib.alhr_forward(cc, P0, P0, P0, NULL, 16, P0, NULL, P0, P0, P0, NULL, 0, NULL) == -3
 
 
 @pytestmark_cpu

@@ -187,6 +187,52 @@ def test_route_stats_match_oracle_counts(torch_dev, name):
         assert st[0, 1, t, 3] == s["count"]
 
 
+ROUTE_SCORE_CASES = [
+    # few pairs per XCD (queries dealt to the XCDs in turn) and eight or more
+    # (contiguous ranges per XCD), and a query count (1 x 5 x 16 = 80) that is
+    # not a multiple of 32 (a block's four waves times the eight XCDs)
+    Workload("score_t1k_b8h8", 2, 8, 8, 1024, 64, "clustered"),
+    Workload("score_t16", 7, 1, 5, 16, 64, "clustered"),
+    Workload("score_t4k_b1h3", 3, 1, 3, 4096, 64, "clustered"),
+]
+
+
+@pytest.mark.parametrize("w", ROUTE_SCORE_CASES, ids=[c.name for c in ROUTE_SCORE_CASES])
+def test_route_scores_and_fused_path(torch_dev, w):
+    """alhr_route's score output holds q . K[j] of every selected key in idx
+    order and 0 in the padding (checked against the oracle's scores on
+    sampled queries of two pairs); routing alone, routing with scores and the
+    fused route + attend give the same index sets."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    Q, K, V, W = host_inputs(w)
+    cfg = w.config()
+    q, k, v, wt = to_dev(torch, dev, Q, K, V, W)
+    say("alhr_route with scores", w.name, "B%d H%d T%d" % (w.B, w.H, w.T))
+    nodes, bud = alhr.alhr_prepare(cfg, q, k, wt)
+    i0, c0 = alhr.alhr_route(cfg, q, k, nodes, bud)
+    i1, c1, sc = alhr.alhr_route(cfg, q, k, nodes, bud, with_score=True)
+    i2, c2, O2 = alhr.alhr_route_attend(cfg, q, k, v, nodes, bud)
+    torch.cuda.synchronize()
+    assert torch.equal(i0, i1) and torch.equal(c0, c1)
+    assert torch.equal(i0, i2) and torch.equal(c0, c2)
+    idx, cnt, sc = (t.cpu().numpy() for t in (i1, c1, sc))
+    ts = np.unique(np.r_[0, 1, 5, w.T // 2 + 3, w.T - 1, np.arange(0, w.T, max(1, w.T // 32))])
+    ts = ts[ts < w.T].astype(np.int32)
+    for (b, h) in ((0, 0), (w.B - 1, w.H - 1)):
+        ref_nodes = oracle.build_tree(K[b, h])
+        S = np.cumsum(K[b, h].astype(np.int64), axis=0)
+        for t in ts:
+            bt, _ = oracle.budget(Q[b, h, t], S[t], W)
+            ridx, rsc, rc, _ = oracle.route(t, bt, Q[b, h, t], K[b, h], ref_nodes, cfg.window,
+                                            cfg.max_budget)
+            assert cnt[b, h, t] == rc
+            np.testing.assert_array_equal(idx[b, h, t], ridx)
+            np.testing.assert_array_equal(sc[b, h, t], rsc)
+    check_pair(w, cfg, Q, K, V, W, {"budget": bud.cpu().numpy(), "idx": idx, "count": cnt,
+                                    "O": O2.cpu().numpy()}, w.B - 1, w.H - 1, ts=ts)
+
+
 def test_repeat_runs_are_bit_identical(torch_dev):
     import learned_tree_routed_amd as alhr
     torch, dev = torch_dev
