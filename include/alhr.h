@@ -201,6 +201,23 @@ alhr_status alhr_forward(const alhr_config *cfg, const int8_t *Q,
                          int32_t *budget, int32_t *idx, int32_t *count,
                          float *O, void *ws, size_t ws_bytes, void *stream);
 
+/* alhr_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * same arguments, checks and results as alhr_forward, without (ws,
+ * ws_bytes): the predictor's scratch is an array of 4 MiB that the library
+ * holds on each GPU it runs on until the process ends, so batch * heads *
+ * ceil(T / 256) must not exceed 32768 when W is given (ALHR_ERR_WORKSPACE
+ * otherwise).  Nothing is allocated or freed.  Every call on one GPU uses
+ * that GPU's array: calls that may overlap on one GPU (different streams)
+ * race and must not be issued.  The stream must belong to the current
+ * device (ALHR_ERR_ARG otherwise). */
+alhr_status alhr_forward_noalloc(const alhr_config *cfg, const int8_t *Q,
+                                 const int8_t *K, const float *V,
+                                 const int8_t *W, int32_t fixed_budget,
+                                 int32_t *nodes, int32_t *budget,
+                                 int32_t *idx, int32_t *count, float *O,
+                                 void *stream);
+
 /* Decode cache set-up: prefix[b, h] = sum_{j < n} K[j] (int32 [batch, heads,
  * d]) read from the tree as the sum of the maximal complete subtrees
  * covering [0, n); 0 <= n <= T (n = 0 gives zeros). */

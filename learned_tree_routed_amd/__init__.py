@@ -24,7 +24,8 @@ __all__ = [
     "alhr_route_stats", "alhr_sparse_attend", "alhr_route_attend", "alhr_forward",
     "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_dense_attend",
     "alhr_status_string", "alhr_last_error", "alhr_version", "alhr_tree_int16_levels",
-    "alhr_split_qk", "alhr_append_decode", "alhr_prepare", "SplitConfig", "EXPORTED",
+    "alhr_split_qk", "alhr_append_decode", "alhr_prepare", "alhr_forward_noalloc", "SplitConfig",
+    "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +37,7 @@ EXPORTED = (
     "alhr_route_stats", "alhr_sparse_attend", "alhr_route_attend", "alhr_forward",
     "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_dense_attend",
     "alhr_status_string", "alhr_last_error", "alhr_version", "alhr_tree_int16_levels",
-    "alhr_split_qk", "alhr_append_decode", "alhr_prepare",
+    "alhr_split_qk", "alhr_append_decode", "alhr_prepare", "alhr_forward_noalloc",
 )
 
 STATUS = {0: "ALHR_OK", -1: "ALHR_ERR_ARG", -2: "ALHR_ERR_OVERFLOW", -3: "ALHR_ERR_DEVICE",
@@ -142,6 +143,7 @@ def load():
         "alhr_sparse_attend": ([cfgp, P, P, P, P, P, P, P], C.c_int),
         "alhr_route_attend": ([cfgp, P, P, P, P, P, i32, P, P, P, P], C.c_int),
         "alhr_forward": ([cfgp, P, P, P, P, i32, P, P, P, P, P, P, sz, P], C.c_int),
+        "alhr_forward_noalloc": ([cfgp, P, P, P, P, i32, P, P, P, P, P, P], C.c_int),
         "alhr_prefix_from_tree": ([cfgp, i32, P, P, P, P], C.c_int),
         "alhr_append": ([cfgp, i32, P, P, P, P, P, P, P], C.c_int),
         "alhr_decode_step": ([cfgp, i32, P, P, P, P, P, P, i32, P, P, P, P, P], C.c_int),
@@ -368,6 +370,29 @@ def alhr_forward(cfg, Q, K, V, W=None, fixed_budget=0, nodes=None, budget=None, 
     _call("alhr_forward", C.byref(cfg.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(W),
           int(fixed_budget), _ptr(nodes), _ptr(budget), _ptr(idx), _ptr(count), _ptr(O),
           _ptr(ws), nbytes, _stream(stream))
+    return {"nodes": nodes, "budget": budget, "idx": idx, "count": count, "O": O}
+
+
+def alhr_forward_noalloc(cfg, Q, K, V, W=None, fixed_budget=0, nodes=None, budget=None, idx=None,
+                         count=None, O=None, stream=None):
+    """alhr_forward with the library's own scratch array instead of a workspace
+    (for callers that cannot allocate: pass every output to allocate nothing
+    here either).  Returns a dict of tensors."""
+    torch = _torch()
+    rows, per_q, idx_shape = _shapes(cfg)
+    _check("Q", Q, torch.int8, rows)
+    _check("K", K, torch.int8, rows, Q.device)
+    _check("V", V, torch.float32, rows, Q.device)
+    nodes = _out(nodes, "nodes", torch.int32, rows, Q.device)
+    idx = _out(idx, "idx", torch.int32, idx_shape, Q.device)
+    count = _out(count, "count", torch.int32, per_q, Q.device)
+    O = _out(O, "O", torch.float32, rows, Q.device)
+    if W is not None:
+        _check("W", W, torch.int8, (cfg.n_classes, 2 * cfg.d), Q.device)
+        budget = _out(budget, "budget", torch.int32, per_q, Q.device)
+    _call("alhr_forward_noalloc", C.byref(cfg.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(W),
+          int(fixed_budget), _ptr(nodes), _ptr(budget), _ptr(idx), _ptr(count), _ptr(O),
+          _stream(stream))
     return {"nodes": nodes, "budget": budget, "idx": idx, "count": count, "O": O}
 
 

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/alhr.h"
@@ -291,12 +292,92 @@ alhr_status alhr_route_attend(const alhr_config* cfg, const int8_t* Q, const int
                         count, O, nullptr, nullptr, true, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The checks and launches of alhr_forward.  ws == nullptr with W given means
+// the library's own scratch array (alhr_forward_noalloc, below).
+alhr_status forward_impl(const char* fn, const alhr_config* cfg, const int8_t* Q,
+                         const int8_t* K, const float* V, const int8_t* W, int32_t fixed_budget,
+                         int32_t* nodes, int32_t* budget, int32_t* idx, int32_t* count, float* O,
+                         void* ws, size_t ws_bytes, bool own_scratch, void* stream);
+
+}  // namespace
+
+extern "C" {
+
 alhr_status alhr_forward(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
                          const float* V, const int8_t* W, int32_t fixed_budget, int32_t* nodes,
                          int32_t* budget, int32_t* idx, int32_t* count, float* O, void* ws,
                          size_t ws_bytes, void* stream)
 {
-    const char* fn = "alhr_forward";
+    return forward_impl("alhr_forward", cfg, Q, K, V, W, fixed_budget, nodes, budget, idx, count,
+                        O, ws, ws_bytes, false, stream);
+}
+
+alhr_status alhr_forward_noalloc(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
+                                 const float* V, const int8_t* W, int32_t fixed_budget,
+                                 int32_t* nodes, int32_t* budget, int32_t* idx, int32_t* count,
+                                 float* O, void* stream)
+{
+    return forward_impl("alhr_forward_noalloc", cfg, Q, K, V, W, fixed_budget, nodes, budget, idx,
+                        count, O, nullptr, 0, true, stream);
+}
+
+}  // extern "C"
+
+// ---- the scratch array of alhr_forward_noalloc -------------------------------
+// A file-scope device array that every GPU the library runs on holds until the
+// process ends (each at its own address).  Host code never passes `scratch`
+// itself to a kernel or copy: on the host the name is a stand-in, not a device
+// address.  The device address comes from hipGetSymbolAddress, taken once per
+// device on the entry point's first call there (that device current) and kept.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, in *out; the device the stream
+// belongs to must be the current one.
+alhr_status scratch_on_current_device(const char* fn, hipStream_t st, void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_status(fn, e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(ALHR_ERR_UNSUPPORTED, "%s: device %d beyond the %d devices served", fn, dev,
+                    kMaxDevices);
+    if (st) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(st, &sdev);
+        if (e != hipSuccess) return device_status(fn, e);
+        if ((int)sdev != dev)
+            return fail(ALHR_ERR_ARG, "%s: the stream belongs to device %d, the current device "
+                                      "is %d", fn, (int)sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return device_status(fn, e);
+        if (!p) return fail(ALHR_ERR_DEVICE, "%s: no device address for the scratch array", fn);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ALHR_OK;
+}
+
+alhr_status forward_impl(const char* fn, const alhr_config* cfg, const int8_t* Q,
+                         const int8_t* K, const float* V, const int8_t* W, int32_t fixed_budget,
+                         int32_t* nodes, int32_t* budget, int32_t* idx, int32_t* count, float* O,
+                         void* ws, size_t ws_bytes, bool own_scratch, void* stream)
+{
     alhr::Shape s;
     if (alhr_status st = check_config(fn, cfg, &s)) return st;
     ALHR_NEED_PTR(Q);
@@ -313,13 +394,25 @@ alhr_status alhr_forward(const alhr_config* cfg, const int8_t* Q, const int8_t* 
                                       "predicted budgets)", fn);
         if (!aligned16(budget))
             return fail(ALHR_ERR_ARG, "%s: argument 'budget' is not 16-byte aligned", fn);
-        if (alhr_status st = check_ws(fn, s, ws, ws_bytes)) return st;
+        if (own_scratch) {
+            if (workspace_bytes(s) > kScratchBytes)
+                return fail(ALHR_ERR_WORKSPACE, "%s: this shape needs %zu bytes of predictor "
+                                                "scratch, beyond the %zu bytes of the library's "
+                                                "array (batch * heads * ceil(T / 256) must not "
+                                                "exceed 32768); use alhr_forward with a workspace",
+                            fn, workspace_bytes(s), kScratchBytes);
+        } else if (alhr_status st = check_ws(fn, s, ws, ws_bytes)) {
+            return st;
+        }
     } else if (fixed_budget < 1 || fixed_budget > cfg->max_budget) {
         return fail(ALHR_ERR_ARG, "%s: fixed_budget = %d must be in [1, max_budget = %d]", fn,
                     fixed_budget, cfg->max_budget);
     }
     hipStream_t st = as_stream(stream);
     (void)hipGetLastError();
+    if (W && own_scratch) {
+        if (alhr_status r = scratch_on_current_device(fn, st, &ws)) return r;
+    }
     // tree and budgets share their launches (alhr_prepare)
     hipError_t e = W ? alhr::launch_prep(s, Q, K, W, nodes, budget, ws, st)
                      : alhr::launch_build(s, K, nodes, st);
@@ -328,6 +421,10 @@ alhr_status alhr_forward(const alhr_config* cfg, const int8_t* Q, const int8_t* 
                                O, nullptr, nullptr, st);
     return device_status(fn, e);
 }
+
+}  // namespace
+
+extern "C" {
 
 alhr_status alhr_dense_attend(const alhr_config* cfg, const int8_t* Q, const int8_t* K,
                               const float* V, float* O, void* stream)
