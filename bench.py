@@ -6,25 +6,29 @@
 A step is one pass of the whole prefill path over one batch: tree build and
 budget prediction (alhr_prepare: the two share their launches), then the
 fused route + attend kernel, i.e. the kernels alhr_forward launches, issued
-as its two ABI calls.  The timed steps are replays of one HIP graph holding
-those calls; an eager loop of the same calls with HIP events on the launch
-stream between them times each part.  Inputs
+as its two ABI calls, each replayed from a HIP graph, with HIP events on the
+launch stream around each replay.  Untimed auxiliary measurements (the
+routing's load counts, the dense baseline, the splitter) run first.  Inputs
 are synthetic and resident in HBM before the timed region.  Prints one JSON
 line:
 
   value     routed queries/s of the whole step (B * H * T queries per step)
-  roofline  the fused route + attend kernel: algorithmic bytes per launch
-            (from the kernel's own per-query load counts) over its average
-            event-timed duration, against 8 TB/s; `traffic` is the rocprofv3
-            FETCH_SIZE + WRITE_SIZE of that kernel (scaled by a plain-copy
-            calibration) when the recorded counters match the current
-            kernel source, else null
+  roofline  the fused route + attend kernel against vector-instruction issue,
+            the bound that limits it (VALU instructions per query from the
+            committed SQ counters x queries / the event-timed launch, against
+            1024 SIMDs x 2.4 GHz / 4); beside it `hbm` (rocprofv3 FETCH_SIZE +
+            WRITE_SIZE bytes past L2, scaled by a plain-copy calibration,
+            against 8 TB/s: an upper bound on the HBM share) and
+            `bytes_touched` (algorithmic bytes); counter figures are null when
+            the committed counters were taken on other source
   cpu_baseline  the single-threaded C oracle on a bounded sample of the same
-            workload, timed on this host (cpu_baseline_all_cores: the same
-            sample with whole pairs spread over up to 16 host threads)
+            workload, pinned to one host core (cpu_baseline_all_cores: the
+            same sample with whole pairs spread over up to 16 host threads)
+  decode    the decode workload (2^17-position, 64 x 16-head cache; append +
+            route + attend per token, 128-token loops) with its HBM roofline
+            and a sampled-pair oracle rate (leave out with --no-decode)
 
-The decode workload (--workload decode) times 128-token decode loops on the
-2^17-position, 64 x 16-head cache: append + route + attend per token.
+--workload decode prints the decode measurement as the line itself.
 """
 from __future__ import annotations
 
@@ -43,8 +47,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "route_attend_t16k_counters.txt")
+PROFILE_DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_t131072_counters.txt")
 ROUTE_SOURCES = [os.path.join(ROOT, "learned_tree_routed_amd", "csrc", f)
-                 for f in ("route.hip", "device.h")]
+                 for f in ("route.hip", "device.h", "append.h")]
 
 
 def route_source_sha():
@@ -87,8 +92,8 @@ def read_issue(kernel_ms, waves):
         if len(parts) >= 2 and parts[0] in ("SQ_INSTS_VALU", "SQ_INSTS_SALU"):
             try:
                 per[parts[0]] = float(parts[1])
-            except ValueError:
-                return None
+            except ValueError:   # prose that starts with a counter name
+                continue
     if sha != route_source_sha() or len(per) != 2:
         return None
     cap = kernel_ms * 1e-3 * CLOCK_GHZ * 1e9 * SIMDS / 4   # wave64 instructions per SIMD slot
@@ -97,13 +102,15 @@ def read_issue(kernel_ms, waves):
             "salu_issue_frac": per["SQ_INSTS_SALU"] * waves / cap}
 
 
-def read_traffic(bytes_unit=1024):
-    """HBM bytes per launch of the route kernel from the committed counter
-    summary, or None when absent or taken on other kernel source."""
-    if not os.path.exists(PROFILE_COUNTERS):
+def read_traffic(bytes_unit=1024, path=None):
+    """HBM bytes per launch of the kernel a committed counter summary covers
+    (the fused route kernel by default), or None when absent or taken on
+    other kernel source."""
+    path = path or PROFILE_COUNTERS
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(PROFILE_COUNTERS):
+    for line in open(path):
         line = line.split("#")[0].strip()
         if ":" in line:
             k, v = line.split(":", 1)
@@ -160,6 +167,32 @@ def host_cores():
     return max(1, min(n, 16))
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+class pinned_to_one_core:
+    """Runs the body on one CPU of this process's set (the calling thread's
+    affinity), restoring the set afterwards; yields the CPU used."""
+
+    def __enter__(self):
+        self.saved = os.sched_getaffinity(0)
+        self.cpu = min(self.saved)
+        os.sched_setaffinity(0, {self.cpu})
+        return self.cpu
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.saved)
+        return False
+
+
 def cpu_baseline(w, Q, K, V, W, stride, threads=1):
     """The C oracle on every stride-th query of every (b, h) pair, each pair
     with its own tree build and prefix.  threads > 1 runs whole pairs on that
@@ -179,19 +212,25 @@ def cpu_baseline(w, Q, K, V, W, stride, threads=1):
         return len(ts)
 
     threads = max(1, min(threads, len(pairs)))
-    t0 = time.perf_counter()
+    core = None
     if threads == 1:
-        n = sum(one(bh) for bh in pairs)
+        with pinned_to_one_core() as core:
+            t0 = time.perf_counter()
+            n = sum(one(bh) for bh in pairs)
+            dt = time.perf_counter() - t0
     else:
+        t0 = time.perf_counter()
         with ThreadPoolExecutor(threads) as ex:
             n = sum(ex.map(one, pairs))
-    dt = time.perf_counter() - t0
+        dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
             "sample": "%s: every %d-th query of all %d (b, h) pairs (%d queries), each pair "
                       "with its full tree build and prefix; C oracle, %s, %.1f s"
                       % (w.name, stride, len(pairs), n,
-                         "single-threaded" if threads == 1 else "%d threads over pairs" % threads,
-                         dt)}
+                         ("single-threaded, pinned to CPU %d" % core) if threads == 1
+                         else "%d threads over pairs" % threads, dt),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "process_cpus": len(os.sched_getaffinity(0))}
 
 
 def bench_splitter(alhr, torch, dev, w, reps=20):
@@ -253,6 +292,52 @@ def capture_step(torch, fn):
     return graph
 
 
+VALU_PEAK_G = SIMDS * CLOCK_GHZ / 4   # 614.4 G wave64 vector instructions/s
+SETTLE_STEPS = 100                     # untimed step replays before the warm-up steps
+
+
+def route_roofline(kern_ms, queries, bytes_launch, issue, traffic):
+    """The fused route + attend kernel against the bound that limits it.
+
+    Its working set (keys, values and the tree of every head, ~70 MiB at
+    T = 16384) stays in the caches, so its re-reads of tree, key and value
+    rows never reach HBM; what limits it is the vector instruction issue: a
+    wave64 VALU instruction holds a SIMD's issue slot for 4 cycles, so the
+    chip issues at most 1024 SIMDs x 2.4 GHz / 4 = 614.4 G of them per
+    second.  `achieved` = the kernel's VALU instructions per query (committed
+    SQ_INSTS_VALU counts for the same source) x queries per launch / the
+    launch's event-timed duration.  Beside it: HBM bytes from the committed
+    FETCH_SIZE / WRITE_SIZE counts over the same duration against 8 TB/s, and
+    the algorithmic bytes touched (row loads counted by the kernel itself),
+    which exceed the HBM peak because the re-reads are cache hits.  The counter
+    bytes are what leaves L2, part of it served by the MALL: an upper bound on
+    the HBM share."""
+    sec = kern_ms * 1e-3
+    out = {"bound": "alu", "achieved": None, "peak": VALU_PEAK_G,
+           "unit": "G wave64 VALU instructions/s", "frac": None, "traffic": traffic,
+           "kernel": "k_route (fused route + attend)", "ms_per_launch": kern_ms,
+           "queries_per_launch": queries}
+    if issue is not None:
+        out["achieved"] = issue["valu_per_query"] * queries / sec / 1e9
+        out["frac"] = out["achieved"] / VALU_PEAK_G
+        out["valu_per_query"] = issue["valu_per_query"]
+        out["salu_per_query"] = issue["salu_per_query"]
+        out["salu_issue_frac"] = issue["salu_per_query"] * queries / sec / 1e9 / VALU_PEAK_G
+    else:
+        out["counters"] = "SQ counters absent or taken on other kernel source: no issue figure"
+    if traffic is not None:
+        gbs = traffic / sec / 1e9
+        out["hbm"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": traffic,
+                      "note": "bytes past L2 (FETCH_SIZE + WRITE_SIZE): served by the 256 MB "
+                              "MALL or by HBM, so an upper bound on the HBM share"}
+    out["bytes_touched"] = {"bytes_per_launch": bytes_launch,
+                            "GBps": bytes_launch / sec / 1e9,
+                            "note": "algorithmic bytes (rows loaded by the kernel); re-reads "
+                                    "are cache hits, so this exceeds what HBM delivers"}
+    return out
+
+
 def bench_prefill(args, torch, dev):
     import learned_tree_routed_amd as alhr
     from synth.workloads import WORKLOADS, host_inputs
@@ -273,46 +358,18 @@ def bench_prefill(args, torch, dev):
     ws = torch.empty(max(alhr.alhr_workspace_bytes(cfg), 256), dtype=torch.uint8, device=dev)
     fixed = w.fixed_budget
 
-    def step(ev):
-        ev[0].record()
-        alhr.alhr_prepare(cfg, q, k, wt, nodes, budget if wt is not None else None,
-                          ws if wt is not None else None)
-        ev[1].record()
-        alhr.alhr_route_attend(cfg, q, k, v, nodes, budget if wt is not None else None, fixed,
-                               idx, count, O)
-        ev[2].record()
+    wb = wt
+    bb = budget if wt is not None else None
+    wsb = ws if wt is not None else None
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(3)]  # noqa: E731
-    for _ in range(args.warmup):
-        step(mk())
+    # Untimed work first: the step once eagerly, the routing's load counts
+    # for the byte model, the dense baseline and the splitter.  It also brings
+    # the GPU to its steady clocks before the timed steps.
+    step_calls(alhr, cfg, q, k, v, wt, nodes, budget, ws, fixed, idx, count, O)
+    _, _, st = alhr.alhr_route_stats(cfg, q, k, nodes, bb, fixed)
     torch.cuda.synchronize()
-    events = [mk() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    eager_ms = (t1 - t0) * 1e3 / args.steps
-    kern = {name: float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
-            for name, a, b in (("prepare_ms", 0, 1), ("route_attend_ms", 1, 2))}
-
-    # The timed figure: the same three calls captured once in a HIP graph and
-    # replayed, so the kernels run back to back instead of waiting on the
-    # host's launches (the eager loop above leaves ~20 us of launch gaps per
-    # step at t16k; its time is kept under diagnostics).
-    graph = capture_step(torch, lambda: step_calls(alhr, cfg, q, k, v, wt, nodes, budget, ws,
-                                                   fixed, idx, count, O))
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # the dense causal baseline on the same inputs (MFMA kernel), for the ratio
+    stats = st.cpu().numpy()
+    del st
     dense_ms = None
     if w.d >= 32:
         Od = torch.empty_like(O)
@@ -325,47 +382,67 @@ def bench_prefill(args, torch, dev):
         torch.cuda.synchronize()
         dense_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev]))
         del Od
-
     # the query/key splitter at this workload's shapes (d_model = heads * d),
     # timed on its own: it precedes the tree path and is not part of a step
     splitter = bench_splitter(alhr, torch, dev, w)
 
-    # load counts of the routing (untimed), for the byte model
-    _, _, st = alhr.alhr_route_stats(cfg, q, k, nodes, budget if wt is not None else None, fixed)
+    # The timed steps: each one replays two HIP graphs, the preparation
+    # (tree + budgets, alhr_prepare) and the fused route + attend
+    # (alhr_route_attend), with HIP events on the launch stream (torch's
+    # current stream, on which the binding launches and the graphs replay)
+    # around each, so the route kernel's duration is measured in the timed
+    # region itself.
+    g_prep = capture_step(torch, lambda: alhr.alhr_prepare(cfg, q, k, wb, nodes, bb, wsb))
+    g_route = capture_step(torch, lambda: alhr.alhr_route_attend(cfg, q, k, v, nodes, bb, fixed,
+                                                                 idx, count, O))
+    # untimed settle phase: the GPU reaches its steady clocks after a few tens
+    # of milliseconds of this kernel (with 5 steps only, the timed route
+    # launches ran 5% slower), then the W warm-up steps
+    for _ in range(SETTLE_STEPS + args.warmup):
+        g_prep.replay()
+        g_route.replay()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
-    stats = st.cpu().numpy()
+    t0 = time.perf_counter()
+    for e in events:
+        e[0].record()
+        g_prep.replay()
+        e[1].record()
+        g_route.replay()
+        e[2].record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    kern = {name: float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
+            for name, a, b in (("prepare_ms", 0, 1), ("route_attend_ms", 1, 2))}
+
     bpl = int(bytes_per_query(stats, cfg, wt is not None).sum())
-    achieved = bpl / (kern["route_attend_ms"] * 1e-3) / 1e9
     counted = args.workload == "t16k" and not args.budget_override
     traffic = read_traffic() if counted else None
-    issue = read_issue(kern["route_attend_ms"], w.B * w.H * w.T) if counted else None
+    queries = w.B * w.H * w.T
+    issue = read_issue(kern["route_attend_ms"], queries) if counted else None
     cnt = count.cpu().numpy()
     bud = budget.cpu().numpy() if wt is not None else np.full_like(cnt, fixed)
-    queries = w.B * w.H * w.T
     out = {
         "metric": "routed queries/sec (build+route+attend) at T=%d; %% of HBM peak" % w.T,
         "value": queries / (ms_step * 1e-3),
         "unit": "queries/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": ms_step, "settle_steps": SETTLE_STEPS,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8/int32 routing, fp32 attention",
+        "dtype": "i8/i32 routing, f32 attention",
         "data": "synthetic (clustered int8 keys, noisy copied queries, seeded)",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "T": w.T, "d": w.d,
                    "window": cfg.window, "max_budget": cfg.max_budget,
                    "budget": ("fixed %d" % fixed) if fixed else "int8 predictor, 32 classes x 3",
                    "queries_per_step": queries,
-                   "launch": "HIP graph of prepare (build + predict) + route/attend per step"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "k_route (fused route + attend)",
-                     "bytes_per_launch": bpl, "ms_per_launch": kern["route_attend_ms"],
-                     "issue": issue},
+                   "launch": "per step: HIP graph of alhr_prepare (build + predict), then HIP "
+                             "graph of alhr_route_attend"},
+        "roofline": route_roofline(kern["route_attend_ms"], queries, bpl, issue, traffic),
         "kernels_ms": kern,
         "dense_baseline": None if dense_ms is None else dense_summary(w, dense_ms, ms_step),
         "splitter": splitter,
         "diagnostics": {"mean_budget": float(bud.mean()), "mean_keys_per_query": float(cnt.mean()),
-                        "eager_ms_per_step": eager_ms,
                         "budget_histogram": {int(v): int(c) for v, c in
                                              zip(*np.unique(bud, return_counts=True))},
                         "mean_tree_rows_loaded_int32": float(stats[..., 0].mean()),
@@ -378,7 +455,14 @@ def bench_prefill(args, torch, dev):
     return out, (w, Q, K, V, W)
 
 
-def bench_decode(args, torch, dev):
+def decode_measure(torch, dev, steps, warmup, with_cpu=True):
+    """The decode workload: 64 sequences x 16 heads, a cache of 2^17 - 128 keys
+    (d = 128, 144 GiB of keys, values and tree, generated on the device), then
+    128 tokens, each one launch of alhr_append_decode (append the key and
+    value, add the key to its ancestors and to the running sum, then predict,
+    route and attend the token's query for every pair).  The 128 launches are
+    one HIP graph; each timed replay starts from the same cache (rebuilt,
+    untimed)."""
     import learned_tree_routed_amd as alhr
     from synth import device as sd
     from synth.workloads import WORKLOADS
@@ -401,7 +485,6 @@ def bench_decode(args, torch, dev):
     cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
     O = torch.empty((B, H, d), dtype=torch.float32, device=dev)
     bud = torch.empty((B, H), dtype=torch.int32, device=dev)
-
     prefix = torch.empty((B, H, d), dtype=torch.int32, device=dev)
 
     def reset():
@@ -412,13 +495,10 @@ def bench_decode(args, torch, dev):
         alhr.alhr_prefix_from_tree(cfg, n0, K, nodes, prefix)
 
     def loop():
-        # one launch per token: append the key and value, then route and attend
         for s in range(S):
             alhr.alhr_append_decode(cfg, n0 + s, ks[s], vs[s], qs[s], K, V, nodes, prefix, Wd, 0,
                                     bud, idx, cnt, O)
 
-    # eager loop once (also the warm-up), then the same 128 launches
-    # captured in a HIP graph; each timed replay starts from a reset cache
     reset()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -430,11 +510,11 @@ def bench_decode(args, torch, dev):
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
         loop()
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         reset()
         graph.replay()
     times = []
-    for _ in range(args.steps):
+    for _ in range(steps):
         reset()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
@@ -445,24 +525,76 @@ def bench_decode(args, torch, dev):
         torch.cuda.synchronize()
         times.append(((time.perf_counter() - t0) * 1e3, ev[0].elapsed_time(ev[1])))
     ms = float(np.mean([t[0] for t in times]))
+    ev_ms = float(np.mean([t[1] for t in times]))
     queries = B * H * S
-    roof = decode_roofline(alhr, torch, dev, w, cfg, K, nodes, qn, Wd, bud, cnt,
-                           float(np.mean([t[1] for t in times])))
-    return {
-        "metric": "routed queries/sec (append+route+attend), decode at T=2^17",
-        "value": queries / (ms * 1e-3), "unit": "queries/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8/int32 routing, fp32 attention",
-        "data": "synthetic (device-generated clustered keys, seeded)",
-        "config": {"workload": "decode", "sequences": B, "heads": H, "T": T, "d": d,
-                   "prefilled": n0, "tokens_per_step": S, "queries_per_step": queries,
-                   "launch": "HIP graph of 128 fused append + decode step launches"},
-        "roofline": roof,
-        "diagnostics": {"mean_keys_last_step": float(cnt.float().mean().item()),
-                        "event_ms_per_step": float(np.mean([t[1] for t in times])),
-                        "eager_ms_per_step": eager_ms},
-    }, None
+    roof, picks = decode_roofline(alhr, torch, dev, w, cfg, K, nodes, qn, Wd, bud, cnt, ev_ms)
+    out = {"metric": "routed queries/sec (append+route+attend), decode at T=2^17",
+           "value": queries / (ms * 1e-3), "unit": "queries/s", "ms_per_step": ms,
+           "steps": steps, "warmup": warmup,
+           "config": {"workload": "decode", "sequences": B, "heads": H, "T": T, "d": d,
+                      "prefilled": n0, "tokens_per_step": S, "queries_per_step": queries,
+                      "launch": "HIP graph of 128 alhr_append_decode launches (one per token)"},
+           "roofline": roof,
+           "diagnostics": {"mean_keys_last_step": float(cnt.float().mean().item()),
+                           "event_ms_per_step": ev_ms, "eager_ms_per_step": eager_ms}}
+    if with_cpu:
+        out["cpu_baseline"] = decode_cpu_baseline(torch, w, cfg, K, V, qn, Wd, picks)
+    del K, V, nodes, kn, vn, qn
+    torch.cuda.empty_cache()
+    return out
+
+
+def decode_cpu_baseline(torch, w, cfg, K, V, qn, Wd, picks):
+    """The oracle replaying the 128 decode steps (append, predictor, route,
+    attend) of sampled (sequence, head) pairs on one pinned host core.  Each
+    pair's prefilled cache and tree are set up untimed, as on the GPU; the
+    key, value and query rows are copied from the device buffers the GPU run
+    used (drawn by the seeded generator)."""
+    import oracle
+    n0, S, T, d = w.n0, w.steps, w.T, w.d
+    W = Wd.cpu().numpy()
+    total, nq = 0.0, 0
+    with pinned_to_one_core() as core:
+        for pidx in picks:
+            b, h = divmod(int(pidx), w.H)
+            Kp = K[b, h].cpu().numpy()
+            Vp = V[b, h].cpu().numpy()
+            Qp = qn[b, h].cpu().numpy()
+            Kc = np.zeros_like(Kp)
+            Kc[:n0] = Kp[:n0]
+            Vc = np.zeros_like(Vp)
+            Vc[:n0] = Vp[:n0]
+            tree = oracle.build_tree(Kc)
+            pre = Kc.astype(np.int64).sum(axis=0)
+            t0 = time.perf_counter()
+            for s in range(S):
+                p = n0 + s
+                oracle.append(p, Kp[p], Vp[p], Kc, Vc, tree, pre)
+                bt, _ = oracle.budget(Qp[s], pre, W, cfg.keys_per_class, cfg.max_budget)
+                ix, _, c, _ = oracle.route(p, bt, Qp[s], Kc, tree, cfg.window, cfg.max_budget)
+                oracle.attend(ix[:c], Qp[s], Kc, Vc, cfg.scale)
+            total += time.perf_counter() - t0
+            nq += S
+            del Kp, Vp, Kc, Vc, tree
+    return {"value": nq / total, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": "decode: %d sampled (sequence, head) pairs x %d steps (append + predictor "
+                      "+ route + attend), prefilled cache built untimed; C oracle, single-"
+                      "threaded, pinned to CPU %d, %.2f s" % (len(picks), S, core, total),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "process_cpus": len(os.sched_getaffinity(0))}
+
+
+def bench_decode(args, torch, dev):
+    d = decode_measure(torch, dev, args.steps, args.warmup, with_cpu=not args.no_cpu_baseline)
+    out = {"metric": d["metric"], "value": d["value"], "unit": d["unit"],
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": d["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "i8/i32 routing, f32 attention",
+           "data": "synthetic (device-generated clustered keys, seeded)",
+           "config": d["config"], "roofline": d["roofline"], "diagnostics": d["diagnostics"]}
+    if "cpu_baseline" in d:
+        out["cpu_baseline"] = d["cpu_baseline"]
+    return out, None
 
 
 def decode_roofline(alhr, torch, dev, w, cfg, K, nodes, qn, Wd, bud, cnt, event_ms_loop,
@@ -506,12 +638,19 @@ def decode_roofline(alhr, torch, dev, w, cfg, K, nodes, qn, Wd, bud, cnt, event_
     bytes_token = (route_b + append_b) * B * H + cfg.n_classes * 2 * d
     ms_token = event_ms_loop / S
     achieved = bytes_token / (ms_token * 1e-3) / 1e9
-    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "k_decode (append + route + attend, one launch per token)",
-            "bytes_per_launch": bytes_token, "ms_per_launch": ms_token,
-            "sample": "load counts of the %d decode queries of %d sampled pairs "
-                      "(alhr_route_stats on the final cache)" % (S * len(picks), len(picks))}
+    traffic = read_traffic(path=PROFILE_DECODE_COUNTERS)
+    out = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+           "kernel": "k_decode (append + route + attend, one launch per token)",
+           "bytes_per_launch": bytes_token, "ms_per_launch": ms_token,
+           "sample": "load counts of the %d decode queries of %d sampled pairs "
+                     "(alhr_route_stats on the final cache)" % (S * len(picks), len(picks))}
+    if traffic is not None:
+        gbs = traffic / (ms_token * 1e-3) / 1e9
+        out["hbm_counted"] = {"achieved": gbs, "frac": gbs / HBM_PEAK_GBS,
+                              "note": "FETCH_SIZE + WRITE_SIZE per launch (committed counters) "
+                                      "over the same duration"}
+    return out, picks
 
 
 def bench_sweep(args, torch, dev):
@@ -648,15 +787,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed warm-up steps (default: 100 for prefill workloads, whose "
-                         "steps are sub-millisecond and which otherwise run before the GPU "
-                         "has reached its steady clocks; 3 for decode)")
+                    help="untimed warm-up steps (default: 20 for prefill workloads, 1 for "
+                         "decode); untimed auxiliary measurements run before them")
     ap.add_argument("--workload", default="t16k", choices=["tiny", "t1k", "t4k", "t16k", "decode"])
     ap.add_argument("--budget-override", type=int, default=0,
                     help="fixed budget for every query instead of the predictor (context runs)")
     ap.add_argument("--cpu-stride", type=int, default=1,
                     help="oracle baseline routes every k-th query of every pair")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="leave out the decode sub-measurement of the default (t16k) run")
+    ap.add_argument("--decode-steps", type=int, default=3,
+                    help="timed 128-token loops of the decode sub-measurement")
     ap.add_argument("--sweep", action="store_true",
                     help="length sweep T = 2^10..2^17 with an exponent fit (JSON line per T)")
     ap.add_argument("--quality", action="store_true",
@@ -666,7 +808,7 @@ def main():
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.warmup is None:
-        args.warmup = 3 if args.workload == "decode" else 100
+        args.warmup = 1 if args.workload == "decode" else 20
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build measures one GPU; the ALHR path shards by (batch, head) "
@@ -709,6 +851,12 @@ def main():
         cores = host_cores()
         if cores > 1:
             out["cpu_baseline_all_cores"] = cpu_baseline(w, Q, K, V, W, args.cpu_stride, cores)
+    if args.workload == "t16k" and not args.budget_override and not args.no_decode:
+        # the decode workload (the HBM-bound case) in the same line, after the
+        # timed prefill steps
+        torch.cuda.empty_cache()
+        out["decode"] = decode_measure(torch, dev, args.decode_steps, 1,
+                                       with_cpu=not args.no_cpu_baseline)
     print(json.dumps(out), flush=True)
 
 

@@ -115,3 +115,39 @@ def test_issue_file_is_read_only_for_the_matching_source(tmp_path, monkeypatch):
 def test_committed_sq_file_parses():
     txt = open(bench.PROFILE_SQ).read()
     assert "route_source_sha" in txt and "SQ_INSTS_VALU" in txt and "SQ_INSTS_SALU" in txt
+
+
+def test_route_roofline_by_hand():
+    """2000 VALU instructions per query, 131072 queries in 0.5 ms: 524.3 G/s
+    against 1024 SIMDs x 2.4 GHz / 4 = 614.4 G/s; 400 MB past L2 in 0.5 ms is
+    800 GB/s of 8000."""
+    issue = {"valu_per_query": 2000.0, "salu_per_query": 1500.0}
+    out = bench.route_roofline(0.5, 131072, 8e9, issue, 4e8)
+    assert out["bound"] == "alu" and out["peak"] == pytest.approx(614.4)
+    assert out["achieved"] == pytest.approx(2000 * 131072 / 0.5e-3 / 1e9)
+    assert out["frac"] == pytest.approx(out["achieved"] / 614.4)
+    assert 0 < out["frac"] <= 1
+    assert out["hbm"]["achieved"] == pytest.approx(800.0) and out["hbm"]["frac"] == pytest.approx(0.1)
+    assert out["bytes_touched"]["GBps"] == pytest.approx(16000.0)
+    none = bench.route_roofline(0.5, 131072, 8e9, None, None)
+    assert none["achieved"] is None and none["frac"] is None and "hbm" not in none
+
+
+def test_single_core_baseline_is_pinned_and_restored():
+    before = os.sched_getaffinity(0)
+    with bench.pinned_to_one_core() as cpu:
+        assert os.sched_getaffinity(0) == {cpu}
+    assert os.sched_getaffinity(0) == before
+    w = WORKLOADS["tiny"]
+    Q, K, V, W = host_inputs(w)
+    out = bench.cpu_baseline(w, Q, K, V, W, 16, 1)
+    assert "pinned to CPU" in out["sample"]
+    assert out["process_cpus"] == len(before) and out["host_cpus"] >= 1
+
+
+def test_committed_counter_summaries_match_the_source():
+    """The committed counter summaries were taken on the current route and
+    decode kernel source (else the bench reports their figures as null)."""
+    assert bench.read_traffic() is not None
+    assert bench.read_traffic(path=bench.PROFILE_DECODE_COUNTERS) is not None
+    assert bench.read_issue(0.5, 131072) is not None
