@@ -234,19 +234,131 @@ def test_route_scores_and_fused_path(torch_dev, w):
 
 
 def test_repeat_runs_are_bit_identical(torch_dev):
+    """Ten runs of every prefill entry point on the same inputs give identical
+    outputs (no race decides a result)."""
     import learned_tree_routed_amd as alhr
     torch, dev = torch_dev
     w = WORKLOADS["t4k"]
     Q, K, V, W = host_inputs(w, B=1, H=4)
     cfg = w.config(batch=1, heads=4)
     q, k, v, wt = to_dev(torch, dev, Q, K, V, W)
-    say("repeat alhr_forward x5, t4k B1 H4")
+    say("repeat alhr_forward / alhr_route / alhr_sparse_attend x10, t4k B1 H4")
     first = alhr.alhr_forward(cfg, q, k, v, wt)
-    for _ in range(4):
+    r0 = alhr.alhr_route(cfg, q, k, first["nodes"], first["budget"], with_score=True)
+    a0 = alhr.alhr_sparse_attend(cfg, q, k, v, first["idx"], first["count"])
+    for _ in range(9):
         again = alhr.alhr_forward(cfg, q, k, v, wt)
+        r1 = alhr.alhr_route(cfg, q, k, again["nodes"], again["budget"], with_score=True)
+        a1 = alhr.alhr_sparse_attend(cfg, q, k, v, again["idx"], again["count"])
         torch.cuda.synchronize()
         for key in ("budget", "idx", "count", "O"):
             assert torch.equal(first[key], again[key]), key
+        assert all(torch.equal(x, y) for x, y in zip(r0, r1))
+        assert torch.equal(a0, a1)
+
+
+def test_launch_geometry_does_not_change_results(torch_dev):
+    """The same pairs computed by different waves, blocks and XCDs: alone in a
+    B1 H8 launch (fewer than 8 pairs per XCD: queries dealt to the XCDs in
+    turn), and as pairs 9..16 of a B9 H8 launch of 72 pairs (contiguous
+    ranges per XCD, other block and wave positions).  Every output of those
+    pairs is identical."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    base = WORKLOADS["t1k"]
+    w8 = Workload("geom8", base.seed, 1, 8, base.T, base.d, base.kind)
+    w72 = Workload("geom72", base.seed, 9, 8, base.T, base.d, base.kind)
+    Q8, K8, V8, W = host_inputs(w8)
+    Q72, K72, V72, _ = host_inputs(w72)
+    # put the 8 pairs of the small launch at batch row 1 of the large one
+    for a, b in ((Q72, Q8), (K72, K8), (V72, V8)):
+        a[1] = b[0]
+    say("launch geometry: B1 H8 vs rows of B9 H8, T1024")
+    small = run_forward(torch, dev, w8, Q8, K8, V8, W)
+    large = run_forward(torch, dev, w72, Q72, K72, V72, W)
+    for key in ("budget", "idx", "count", "O"):
+        np.testing.assert_array_equal(small[key][0], large[key][1], err_msg=key)
+    l16 = alhr.alhr_tree_int16_levels(w8.config())
+    for h in range(8):
+        np.testing.assert_array_equal(decode_tree(small["nodes"][0, h], l16)[1:],
+                                      decode_tree(large["nodes"][1, h], l16)[1:])
+
+
+def test_sparse_attend_skips_invalid_caller_indices(torch_dev):
+    """Caller-supplied index sets with positions outside [0, T) (negative, or
+    T and beyond) and counts outside [0, max_budget]: the count is clamped,
+    invalid positions are left out of the softmax, and the output equals the
+    oracle's attention over the valid positions (0 when none is valid)."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    w = Workload("attend_invalid", 31, 1, 2, 512, 64, "clustered")
+    Q, K, V, _ = host_inputs(w)
+    cfg = w.config(max_budget=32)
+    rng = np.random.default_rng(31)
+    T, mb = w.T, cfg.max_budget
+    idx = rng.integers(0, T, size=(1, 2, T, mb)).astype(np.int32)
+    bad = rng.random(size=idx.shape) < 0.25
+    idx[bad] = rng.choice(np.array([-1, -7, T, T + 5, 1 << 30, -(1 << 30)], dtype=np.int32),
+                          size=int(bad.sum()))
+    cnt = rng.integers(-3, mb + 8, size=(1, 2, T)).astype(np.int32)
+    idx[0, 0, 7, :] = -1            # a query with no valid position at all
+    cnt[0, 0, 7] = 5
+    q, k, v, ti, tc = to_dev(torch, dev, Q, K, V, idx, cnt)
+    say("alhr_sparse_attend with invalid caller indices, T512 d64")
+    O = alhr.alhr_sparse_attend(cfg, q, k, v, ti, tc)
+    torch.cuda.synchronize()
+    O = O.cpu().numpy()
+    worst = 0.0
+    for h in range(2):
+        for t in range(T):
+            c = int(np.clip(cnt[0, h, t], 0, mb))
+            sel = idx[0, h, t, :c]
+            sel = sel[(sel >= 0) & (sel < T)]
+            if len(sel) == 0:
+                assert not O[0, h, t].any(), (h, t)
+                continue
+            ref = oracle.attend(sel, Q[0, h, t], K[0, h], V[0, h], cfg.scale)
+            worst = max(worst, float(np.abs(O[0, h, t] - ref).max()))
+    assert worst <= ATOL, worst
+
+
+def test_route_d64_two_cover_passes_at_2_17(torch_dev):
+    """d = 64 at T = 2^17 (B1 H8, the length sweep's top point).  A wave
+    scores 16 rows per pass at d = 64 and the cover of [0, m) has a root on
+    every set bit of m, levels 0..16 here, so every query with m >= 2^16 takes
+    a second cover pass for its level-16 root.  Sampled queries of two pairs
+    (the first and last, m = 2^16 exactly, the m below T with the most set
+    bits, random) against the oracle."""
+    import learned_tree_routed_amd as alhr
+    from synth import device as sd
+    from synth.workloads import pair_keys, pair_query_rows, pair_value_rows
+    torch, dev = torch_dev
+    T, d = 1 << 17, 64
+    w = Workload("t2e17", 8, 1, 8, T, d, "clustered")
+    cfg = w.config()
+    shape = (1, 8, T, d)
+    K = sd.keys_(torch.empty(shape, dtype=torch.int8, device=dev), w.seed)
+    Qd = sd.queries_(torch.empty(shape, dtype=torch.int8, device=dev), w.seed)
+    V = sd.values_(torch.empty(shape, dtype=torch.float32, device=dev), w.seed)
+    W = synth.predictor_weights(w.seed, w.n_classes, d)
+    say("alhr_forward B1 H8 T2^17 d64 (two cover passes)")
+    out = alhr.alhr_forward(cfg, Qd, K, V, torch.from_numpy(W).to(dev))
+    torch.cuda.synchronize()
+    # t = m + 3 when the window holds 4 keys; m = 2^17 - 5 has 15 set bits
+    many = [m + 3 for m in range(T - 64, T - 3) if bin(m).count("1") >= 15]
+    rng = np.random.default_rng(w.seed)
+    ts = np.unique(np.r_[0, 1, 2, 3, 4, 65535, 65538, 65539, 65540, T - 2, T - 1, many,
+                         rng.integers(1 << 16, T, 48)]).astype(np.int32)
+    for h in (0, 5):
+        Kp = pair_keys(w, 0, h)
+        Qp = pair_query_rows(w, 0, h, np.arange(T))
+        Vp = pair_value_rows(w, 0, h, np.arange(T))
+        ref = oracle.pair_forward(Qp, Kp, Vp, W=W, window=cfg.window, scale=cfg.scale, ts=ts)
+        np.testing.assert_array_equal(out["budget"][0, h].cpu().numpy()[ts], ref["budget"])
+        np.testing.assert_array_equal(out["count"][0, h].cpu().numpy()[ts], ref["count"])
+        np.testing.assert_array_equal(out["idx"][0, h].cpu().numpy()[ts], ref["idx"])
+        err = np.abs(out["O"][0, h].cpu().numpy()[ts] - ref["O"]).max()
+        assert err <= ATOL, (h, err)
 
 
 # ---------------------------------------------------------------- edges ---
