@@ -25,7 +25,7 @@ __all__ = [
     "alhr_prefix_from_tree", "alhr_append", "alhr_decode_step", "alhr_dense_attend",
     "alhr_status_string", "alhr_last_error", "alhr_version", "alhr_tree_int16_levels",
     "alhr_split_qk", "alhr_append_decode", "alhr_prepare", "alhr_forward_noalloc", "SplitConfig",
-    "EXPORTED",
+    "EXPORTED", "load_geometry_variant",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -122,15 +122,8 @@ def lib_path():
     return _LIB_PATH
 
 
-def load():
-    """Load libalhr.so; raises if it has not been built."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
-        raise RuntimeError("libalhr.so is not built at %s: run `python -m "
-                           "learned_tree_routed_amd.build` (no fallback path exists)" % _LIB_PATH)
-    lib = C.CDLL(_LIB_PATH)
+def _bind(lib):
+    """Give every exported function of a loaded libalhr its C signature."""
     P, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
     cfgp = C.POINTER(CConfig)
     sigs = {
@@ -159,8 +152,30 @@ def load():
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = res
-    _lib = lib
     return lib
+
+
+def load():
+    """Load libalhr.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libalhr.so is not built at %s: run `python -m "
+                           "learned_tree_routed_amd.build` (no fallback path exists)" % _LIB_PATH)
+    _lib = _bind(C.CDLL(_LIB_PATH))
+    return _lib
+
+
+def load_geometry_variant(waves):
+    """A copy of libalhr.so built with ``waves`` (2 or 8) queries per prefill
+    routing workgroup, bound like load()'s; for checking that results do not
+    depend on the launch geometry.  Raises if it has not been built."""
+    from .build import GEOMETRY_VARIANTS
+    path = GEOMETRY_VARIANTS[waves]
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built: run `python -m learned_tree_routed_amd.build`" % path)
+    return _bind(C.CDLL(path))
 
 
 # ----------------------------------------------------------------- helpers --

@@ -62,13 +62,47 @@ def _link(objs, out):
     os.replace(tmp, out)
 
 
-def build_alhr(jobs=8):
+# Copies of libalhr.so whose prefill routing kernels run 2 or 8 queries per
+# workgroup instead of 4 (route.hip built with ALHR_ROUTE_WAVES_PER_BLOCK).
+# Only the launch-geometry test loads them: the same queries at other block
+# and wave positions must give identical results.
+GEOMETRY_VARIANTS = {2: os.path.join(PKG, "libalhr_wpb2.so"),
+                     8: os.path.join(PKG, "libalhr_wpb8.so")}
+
+
+def _objects():
+    return [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in SOURCES]
+
+
+def _variant_object(waves):
+    return os.path.join(BUILD_DIR, "route_wpb%d.o" % waves)
+
+
+def _compile_variant(waves):
+    return _run([HIPCC] + FLAGS + EXTRA["route.hip"] +
+                ["-DALHR_ROUTE_WAVES_PER_BLOCK=%d" % waves, "-c",
+                 os.path.join(CSRC, "route.hip"), "-o", _variant_object(waves)])
+
+
+def _link_variant(waves):
+    objs = [_variant_object(waves) if s == "route.hip" else o for s, o in zip(SOURCES, _objects())]
+    _link(objs, GEOMETRY_VARIANTS[waves])
+    return GEOMETRY_VARIANTS[waves]
+
+
+def build_alhr(jobs=8, variants=False):
+    """libalhr.so; with ``variants`` also the launch-geometry copies."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in SOURCES]
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        list(ex.map(_compile, [os.path.join(CSRC, s) for s in SOURCES], objs))
-    _link(objs, LIB)
-    return LIB
+        futs = [ex.submit(_compile, os.path.join(CSRC, s), o) for s, o in zip(SOURCES, _objects())]
+        if variants:
+            futs += [ex.submit(_compile_variant, w) for w in GEOMETRY_VARIANTS]
+        for f in futs:
+            f.result()
+    _link(_objects(), LIB)
+    if variants:
+        return [LIB] + [_link_variant(w) for w in GEOMETRY_VARIANTS]
+    return [LIB]
 
 
 def build_synth():
@@ -81,9 +115,9 @@ def build_synth():
 
 def build_all(jobs=8):
     with cf.ThreadPoolExecutor(max_workers=2) as ex:
-        a = ex.submit(build_alhr, jobs)
+        a = ex.submit(build_alhr, jobs, True)
         b = ex.submit(build_synth)
-        return a.result(), b.result()
+        return tuple(a.result()) + (b.result(),)
 
 
 if __name__ == "__main__":

@@ -39,7 +39,16 @@ namespace {
 
 constexpr int kMaxBudget = 128;
 constexpr int kSlots = 256;             // 2 * (kMaxBudget - 1) candidates fit
-constexpr int kWavesPerBlock = 4;
+// Waves (queries) per workgroup of the prefill routing and attention kernels.
+// A build option only so that the same queries can be run at other launch
+// geometries (the results must not depend on it); 4 is the product setting.
+#ifndef ALHR_ROUTE_WAVES_PER_BLOCK
+#define ALHR_ROUTE_WAVES_PER_BLOCK 4
+#endif
+constexpr int kWavesPerBlock = ALHR_ROUTE_WAVES_PER_BLOCK;
+static_assert(kWavesPerBlock == 1 || kWavesPerBlock == 2 || kWavesPerBlock == 4 ||
+                  kWavesPerBlock == 8,
+              "1, 2, 4 or 8 waves per workgroup");
 constexpr int kThreads = kWavesPerBlock * kWave;
 constexpr int kMaxClasses = 32;
 

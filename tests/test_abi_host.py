@@ -50,6 +50,18 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) <= exported
 
 
+@pytest.mark.parametrize("waves", [2, 8])
+def test_geometry_variants_export_the_same_symbols(waves):
+    """The launch-geometry copies of the library (route kernels at 2 or 8
+    queries per workgroup) load and export every declared function."""
+    from learned_tree_routed_amd.build import GEOMETRY_VARIANTS
+    lib = alhr.load_geometry_variant(waves)
+    out = subprocess.run(["nm", "-D", "--defined-only", GEOMETRY_VARIANTS[waves]],
+                         capture_output=True, text=True, check=True).stdout
+    assert set(declared_functions()) <= set(re.findall(r" T (alhr_\w+)", out))
+    assert lib.alhr_version() == alhr.load().alhr_version()
+
+
 def test_status_strings_and_version():
     assert alhr.alhr_version() >= 100
     for code, name in alhr.STATUS.items():

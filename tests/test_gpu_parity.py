@@ -284,6 +284,39 @@ def test_launch_geometry_does_not_change_results(torch_dev):
                                       decode_tree(large["nodes"][1, h], l16)[1:])
 
 
+@pytest.mark.parametrize("waves", [2, 8])
+def test_waves_per_workgroup_do_not_change_results(torch_dev, monkeypatch, waves):
+    """The prefill routing and attention kernels built with 2 or 8 queries per
+    workgroup instead of 4 (libalhr_wpb2.so, libalhr_wpb8.so): identical
+    budgets, index sets, counts, scores and outputs for alhr_forward,
+    alhr_route and alhr_sparse_attend, at 64 pairs (contiguous query ranges
+    per XCD) and at 4 pairs (queries dealt to the XCDs in turn)."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    variant = alhr.load_geometry_variant(waves)
+    for name, B, H in (("t1k", 8, 8), ("t4k", 1, 4)):
+        w = WORKLOADS[name]
+        Q, K, V, W = host_inputs(w, B=B, H=H)
+        cfg = w.config(batch=B, heads=H)
+        q, k, v, wt = to_dev(torch, dev, Q, K, V, W)
+
+        def run():
+            f = alhr.alhr_forward(cfg, q, k, v, wt)
+            r = alhr.alhr_route(cfg, q, k, f["nodes"], f["budget"], with_score=True)
+            a = alhr.alhr_sparse_attend(cfg, q, k, v, f["idx"], f["count"])
+            torch.cuda.synchronize()
+            return [f[x] for x in ("budget", "idx", "count", "O")] + list(r) + [a]
+
+        say("libalhr.so (4 waves per workgroup)", name, "B%d H%d" % (B, H))
+        ref = run()
+        say("libalhr_wpb%d.so" % waves, name, "B%d H%d" % (B, H))
+        with monkeypatch.context() as m:
+            m.setattr(alhr, "_lib", variant)
+            got = run()
+        for i, (a, b) in enumerate(zip(ref, got)):
+            assert torch.equal(a, b), (name, i)
+
+
 def test_sparse_attend_skips_invalid_caller_indices(torch_dev):
     """Caller-supplied index sets with positions outside [0, T) (negative, or
     T and beyond) and counts outside [0, max_budget]: the count is clamped,
