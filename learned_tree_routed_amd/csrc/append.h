@@ -81,72 +81,80 @@ __device__ __forceinline__ void append_columns(int pair, int g, const int8_t* __
     *pre = make_int4(p.x + kv.x, p.y + kv.y, p.z + kv.z, p.w + kv.w);
 }
 
-// The same append done by a whole workgroup of NT threads for one pair:
-// thread t owns column chunk g = t % (d/4) at the levels lgrp + 1,
-// lgrp + 1 + groups, ... (lgrp = t / (d/4), groups = NT / (d/4)), so each
-// thread holds one to a few ancestor cells instead of all L; the level-group
-// 0 threads also store the key and value rows and update the running sum.
-// Threads g and g ^ 1 of a level group are adjacent lanes (d/4 is even and
-// divides 64).  Every thread of the workgroup calls it.
+// The append spread over NT threads of a workgroup (thread index tid < NT)
+// for one pair, in two halves so that the caller's own loads can be in
+// flight with these: load() reads the new key and this thread's ancestor
+// cells, store() writes the cells with the key added.  No store comes before
+// a load: a wave's loads and stores share one completion counter, so a
+// store issued first would hold up the loads.  The key and value rows at pos
+// are the caller's to store.  Thread tid owns column chunk
+// g = tid % (d/4) at the levels lgrp + 1, lgrp + 1 + groups, ...
+// (lgrp = tid / (d/4), groups = NT / (d/4)); threads g and g ^ 1 of a level
+// group are adjacent lanes (d/4 is even and divides 64).  The running sum
+// is not touched here: its owner forms S[pos] = S[pos-1] + k_new itself.
 template <int D, int NT>
-__device__ __forceinline__ void append_columns_spread(int pair, const int8_t* __restrict__ k_new,
-                                                      const float* __restrict__ v_new,
-                                                      int8_t* __restrict__ K,
-                                                      float* __restrict__ V,
-                                                      int32_t* __restrict__ nodes,
-                                                      int32_t* __restrict__ prefix, int T, int L,
-                                                      int l16, int pos)
-{
-    constexpr int C4 = D / 4, NG = NT / C4;
+struct SpreadAppend {
+    static constexpr int C4 = D / 4, NG = NT / C4;
+    static constexpr int kPer = (kMaxLevels + NG - 1) / NG;   // levels per thread at most
     static_assert(NT % C4 == 0 && 64 % C4 == 0 && C4 % 2 == 0, "column chunks tile the waves");
-    const int g = threadIdx.x % C4, lgrp = threadIdx.x / C4;
-    const int kw = reinterpret_cast<const int*>(k_new)[(size_t)pair * C4 + g];
-    const int4 kv = make_int4(sbyte(kw, 0), sbyte(kw, 1), sbyte(kw, 2), sbyte(kw, 3));
-    const int kw_partner = __shfl_xor(kw, 1);
-    const int kw_even = (g & 1) ? kw_partner : kw, kw_odd = (g & 1) ? kw : kw_partner;
-    if (lgrp == 0) {
-        const size_t row = (size_t)pair * T + pos;
-        reinterpret_cast<int*>(K)[row * C4 + g] = kw;
-        reinterpret_cast<float4*>(V)[row * C4 + g] =
-            reinterpret_cast<const float4*>(v_new)[(size_t)pair * C4 + g];
-        int4* pre = reinterpret_cast<int4*>(prefix) + (size_t)pair * C4 + g;
-        const int4 p = *pre;
-        *pre = make_int4(p.x + kv.x, p.y + kv.y, p.z + kv.z, p.w + kv.w);
-    }
-    int32_t* tree = nodes + (size_t)pair * T * D;
-    constexpr int kPer = (kMaxLevels + NG - 1) / NG;   // levels per thread at most
-    int4* cell_at[kPer];
     int4 cells[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int l0 = lgrp + 1 + k * NG;
-        const int l = l0 < L ? l0 : L;   // clamped: extra cells re-read and rewrite the root
+    int kw;
+
+    __device__ __forceinline__ static int4* cell(int32_t* tree, int T, int l16, int pos, int l,
+                                                 int g)
+    {
         const size_t r = (size_t)((T >> l) + (pos >> l));
-        cell_at[k] = l <= l16
+        return l <= l16
             ? reinterpret_cast<int4*>(const_cast<int32_t*>(tree_row16<D>(tree, T, l16, r))) +
                   (g >> 1)
             : reinterpret_cast<int4*>(tree + r * D) + wide_slot<D>(g);
-        cells[k] = *cell_at[k];
     }
+
+    __device__ __forceinline__ void load(int tid, int pair, const int8_t* __restrict__ k_new,
+                                         const int32_t* __restrict__ nodes, int T, int L, int l16,
+                                         int pos)
+    {
+        const int g = tid % C4, lgrp = tid / C4;
+        kw = reinterpret_cast<const int*>(k_new)[(size_t)pair * C4 + g];
+        int32_t* tree = const_cast<int32_t*>(nodes) + (size_t)pair * T * D;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int l0 = lgrp + 1 + k * NG;
-        const int l = l0 < L ? l0 : L;
-        const int4 c = cells[k];
-        const int4 wide = make_int4(c.x + kv.x, c.y + kv.y, c.z + kv.z, c.w + kv.w);
-        const int4 narrow = make_int4(
-            pack16(lo16(c.x) + sbyte(kw_even, 0), hi16(c.x) + sbyte(kw_even, 1)),
-            pack16(lo16(c.y) + sbyte(kw_even, 2), hi16(c.y) + sbyte(kw_even, 3)),
-            pack16(lo16(c.z) + sbyte(kw_odd, 0), hi16(c.z) + sbyte(kw_odd, 1)),
-            pack16(lo16(c.w) + sbyte(kw_odd, 2), hi16(c.w) + sbyte(kw_odd, 3)));
-        const bool nar = l <= l16;
-        // several threads may clamp to the root: only the one whose level is
-        // really L (or, past L, none) writes it
-        if (l0 <= L)
-            *cell_at[k] = make_int4(nar ? narrow.x : wide.x, nar ? narrow.y : wide.y,
-                                    nar ? narrow.z : wide.z, nar ? narrow.w : wide.w);
+        for (int k = 0; k < kPer; ++k) {
+            const int l0 = lgrp + 1 + k * NG;
+            const int l = l0 < L ? l0 : L;   // clamped: extra cells re-read the root
+            cells[k] = *cell(tree, T, l16, pos, l, g);
+        }
     }
-}
+
+    __device__ __forceinline__ void store(int tid, int pair, int32_t* __restrict__ nodes, int T,
+                                          int L, int l16, int pos) const
+    {
+        const int g = tid % C4, lgrp = tid / C4;
+        const int4 kv = make_int4(sbyte(kw, 0), sbyte(kw, 1), sbyte(kw, 2), sbyte(kw, 3));
+        // key bytes of the even and the odd thread of this thread's pair g, g ^ 1
+        const int kw_partner = __shfl_xor(kw, 1);
+        const int kw_even = (g & 1) ? kw_partner : kw, kw_odd = (g & 1) ? kw : kw_partner;
+        int32_t* tree = nodes + (size_t)pair * T * D;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int l0 = lgrp + 1 + k * NG;
+            const int l = l0 < L ? l0 : L;
+            const int4 c = cells[k];
+            const int4 wide = make_int4(c.x + kv.x, c.y + kv.y, c.z + kv.z, c.w + kv.w);
+            const int4 narrow = make_int4(
+                pack16(lo16(c.x) + sbyte(kw_even, 0), hi16(c.x) + sbyte(kw_even, 1)),
+                pack16(lo16(c.y) + sbyte(kw_even, 2), hi16(c.y) + sbyte(kw_even, 3)),
+                pack16(lo16(c.z) + sbyte(kw_odd, 0), hi16(c.z) + sbyte(kw_odd, 1)),
+                pack16(lo16(c.w) + sbyte(kw_odd, 2), hi16(c.w) + sbyte(kw_odd, 3)));
+            const bool nar = l <= l16;
+            // several threads may clamp to the root: only the one whose level is
+            // really L (or, past L, none) writes it
+            if (l0 <= L)
+                *cell(tree, T, l16, pos, l, g) =
+                    make_int4(nar ? narrow.x : wide.x, nar ? narrow.y : wide.y,
+                              nar ? narrow.z : wide.z, nar ? narrow.w : wide.w);
+        }
+    }
+};
 
 }  // namespace appendk
 }  // namespace alhr

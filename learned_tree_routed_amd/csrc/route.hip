@@ -804,85 +804,323 @@ __global__ __launch_bounds__(kThreads) void k_attend(const int8_t* __restrict__ 
     store_output<D>(O + qrow * D, attend_selected<D, true>(sm, C, T, scale, V + (size_t)pair * T * D));
 }
 
-// ---- decode: one wave per pair, query at position pos --------------------
-// Budget from W . [q; S[pos]]: lane c < n_classes forms z_c, then an argmax
-// over (z, lowest class) keys.
+// ---- decode: one workgroup per pair, query at position pos ---------------
+// Decode has one query per (sequence, head) and step, so the grid is small
+// and each query's chain of dependent steps decides the latency: budget,
+// cover of [0, m), about log2(T) descent rounds, attention.  A workgroup of
+// kDecodeWaves waves serves one query.
+//
+// The first phase runs three independent parts side by side: waves 0-3
+// predict the budget and (fused append) store the new key and value rows and
+// add the key to its ancestors; waves 4-7 score the cover roots and the
+// window of neighbours.  None needs another's result: the cover roots, and
+// every node below them, lie in [0, m) with m <= pos, so the append changes
+// none of them; the window is scored for the widest n it can have before
+// the budget is known (whenever r > 0 the cover's m is that window's); and
+// the predictor forms S[pos] itself.  Each descent round then has wave 0
+// select the beam between two barriers while every wave scores a share of
+// the round's rows (kDecodeWaves x 64 / (d/16) rows per pass, two passes
+// loaded together), and all waves share the value gather.
+constexpr int kDecodeWaves = 8;
+constexpr int kPredictWaves = 4;
+constexpr int kPredictThreads = kPredictWaves * kWave;
+constexpr int kCoverWaves = kDecodeWaves - kPredictWaves;
+
+struct BlockShared {
+    WaveLds sm;
+    float4 red[kDecodeWaves][kWave];   // per-wave partial output rows
+    uint64_t pbest[kPredictWaves];      // per-wave best (logit, class) key
+    int nsc[kMaxBudget];                // window scores, positions t+1-nw .. t
+    int4 snew[256 / 4];                 // S[pos] with the new key added (d <= 256)
+    int nb, inner;
+    float z;
+};
+
+// The budget predictor (ALHR README, "Inference stage": a linear layer on the
+// query and the causal key sum, argmax over the budget classes) for one
+// decode query, spread over threads u < kPredictThreads: thread u takes
+// class c = u / TPC and the 16-column chunks p, p + TPC, ... (p = u % TPC)
+// of both halves of the class row [Wq | Ws] against [q; S].  The logit is
+// summed over the class's TPC lanes and each wave keeps its best key (larger
+// logit, then lower class) in pbest.  With APPEND the stored running sum is
+// S[pos-1] and S = S[pos-1] + k_new; class 0's threads leave S in snew, for
+// the caller to store once no thread reads the old sum.  All sums are int32
+// (two's complement), so the order of the additions does not change a logit.
+// With APPEND the same threads also form q . k_new, the window score of
+// position t (its key row is not stored yet), into nsc[nw - 1].
 template <int D>
-__device__ __forceinline__ int predict_one(const int8_t* __restrict__ q,
-                                           const int32_t* __restrict__ pre,
-                                           const int8_t* __restrict__ W, int nc, int kpc, int cap)
+struct PredictSplit {
+    static constexpr int TPC = D / 16 < 8 ? D / 16 : 8;   // threads per class
+    static constexpr int CPT = D / 16 / TPC;                // chunks per thread
+};
+
+template <int D, bool APPEND>
+__device__ __forceinline__ void predict_block(int u, const int8_t* __restrict__ qp,
+                                              const int32_t* __restrict__ pre,
+                                              const int8_t* __restrict__ kn,
+                                              const int8_t* __restrict__ W, int nc, int nw,
+                                              BlockShared& bs)
 {
-    const int lane = lane_id();
-    int z = 0;
-    if (lane < nc) {
-        const int* w = reinterpret_cast<const int*>(W + (size_t)lane * 2 * D);
-        const int* qw = reinterpret_cast<const int*>(q);
-        for (int i = 0; i < D / 4; ++i) z = dot4_i8(w[i], qw[i], z);
-        for (int i = 0; i < D / 4; ++i) {
-            const int ws = w[D / 4 + i];
+    constexpr int TPC = PredictSplit<D>::TPC, CPT = PredictSplit<D>::CPT;
+    static_assert(kMaxClasses * TPC <= kPredictThreads, "one class per thread group");
+    const int c = u / TPC, p = u % TPC;
+    const bool act = c < nc;
+    const int8_t* wrow = W + (size_t)(act ? c : 0) * 2 * D;   // inactive: class 0, unused
+    int z = 0, self = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) z += sbyte(ws, e) * pre[4 * i + e];
+    for (int k = 0; k < CPT; ++k) {
+        const int ch = p + k * TPC;   // columns 16 ch .. 16 ch + 15
+        const int4 wq = reinterpret_cast<const int4*>(wrow)[ch];
+        const int4 ws = reinterpret_cast<const int4*>(wrow + D)[ch];
+        const int4 qq = reinterpret_cast<const int4*>(qp)[ch];
+        int4 sv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[e] = reinterpret_cast<const int4*>(pre)[4 * ch + e];
+        if constexpr (APPEND) {
+            const int4 kk = reinterpret_cast<const int4*>(kn)[ch];
+            const int kw[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sv[e] = make_int4(sv[e].x + sbyte(kw[e], 0), sv[e].y + sbyte(kw[e], 1),
+                                  sv[e].z + sbyte(kw[e], 2), sv[e].w + sbyte(kw[e], 3));
+            self = dot4_i8(qq.x, kk.x, self);
+            self = dot4_i8(qq.y, kk.y, self);
+            self = dot4_i8(qq.z, kk.z, self);
+            self = dot4_i8(qq.w, kk.w, self);
+        }
+        z = dot4_i8(wq.x, qq.x, z);
+        z = dot4_i8(wq.y, qq.y, z);
+        z = dot4_i8(wq.z, qq.z, z);
+        z = dot4_i8(wq.w, qq.w, z);
+        const int wsw[4] = {ws.x, ws.y, ws.z, ws.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            z += sbyte(wsw[e], 0) * sv[e].x;
+            z += sbyte(wsw[e], 1) * sv[e].y;
+            z += sbyte(wsw[e], 2) * sv[e].z;
+            z += sbyte(wsw[e], 3) * sv[e].w;
+            if (APPEND && c == 0) bs.snew[4 * ch + e] = sv[e];
         }
     }
-    const uint64_t key = lane < nc ? (((uint64_t)((uint32_t)z ^ 0x80000000u) << 32) |
-                                      (uint32_t)(kMaxClasses - lane))
-                                   : 0ull;
+    z = group_sum<TPC>(z);
+    if constexpr (APPEND) {
+        self = group_sum<TPC>(self);
+        if (u == 0) bs.nsc[nw - 1] = self;
+    }
+    const uint64_t key = act && p == 0 ? (((uint64_t)((uint32_t)z ^ 0x80000000u) << 32) |
+                                          (uint32_t)(kMaxClasses - c))
+                                       : 0ull;
     const uint64_t best = wave_max(key);
+    if (lane_id() == 0) bs.pbest[u / kWave] = best;
+}
+
+// q . k_new into nsc[nw - 1] when no predictor runs (fixed budget with
+// APPEND): the threads u < TPC of the predictor's split, class 0's.
+template <int D>
+__device__ __forceinline__ void own_score(int u, const int8_t* __restrict__ qp,
+                                          const int8_t* __restrict__ kn, int nw, BlockShared& bs)
+{
+    constexpr int TPC = PredictSplit<D>::TPC, CPT = PredictSplit<D>::CPT;
+    if (u >= TPC) return;   // whole groups of TPC lanes: the sum below stays inside them
+    int self = 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int ch = u + k * TPC;
+        const int4 qq = reinterpret_cast<const int4*>(qp)[ch];
+        const int4 kk = reinterpret_cast<const int4*>(kn)[ch];
+        self = dot4_i8(qq.x, kk.x, self);
+        self = dot4_i8(qq.y, kk.y, self);
+        self = dot4_i8(qq.z, kk.z, self);
+        self = dot4_i8(qq.w, kk.w, self);
+    }
+    self = group_sum<TPC>(self);
+    if (u == 0) bs.nsc[nw - 1] = self;
+}
+
+__device__ __forceinline__ int budget_from_best(const BlockShared& bs, int kpc, int cap)
+{
+    uint64_t best = bs.pbest[0];
+#pragma unroll
+    for (int w = 1; w < kPredictWaves; ++w) best = bs.pbest[w] > best ? bs.pbest[w] : best;
     const int cls = kMaxClasses - (int)(uint32_t)best;
     const int b = kpc * (cls + 1);
     return b < cap ? b : cap;
 }
 
-// Decode has one query per (sequence, head) and step, so the grid is small
-// and each query's ~log2(T) dependent rounds decide the latency.  A workgroup
-// of kDecodeWaves waves serves one query: every wave scores a share of a
-// round's rows (one pass covers 8 x 64 / (d/16) rows), wave 0 selects between
-// two barriers, and all waves share the value gather.
-constexpr int kDecodeWaves = 8;
-
-struct BlockShared {
-    WaveLds sm;
-    float4 red[kDecodeWaves][kWave];   // per-wave partial output rows
-    int nb, inner, budget;
-    float z;
-};
-
+// q . node with every kind of row loaded at once and no branch: four 16-byte
+// loads from the tree table (an int32 row uses all four, an int16 row the
+// first two) and one from the key rows.  Slots a node does not use read row
+// 0, which is allocated and never used.  The first phase's rows are of mixed kinds (cover roots at
+// every level, window keys); this way they cost one memory round trip, not
+// one per kind.  Inactive lanes give 0.
 template <int D, bool MUL24>
-__device__ int route_query_block(const int32_t* __restrict__ nodes_pair,
-                                 const int8_t* __restrict__ keys_pair, int T, int L, int l16,
-                                 int t, int B, int window, const QueryRegs<D>& q,
-                                 BlockShared& bs)
+__device__ __forceinline__ int score_node_flat(gbyte* nbase, gbyte* kbase, int T, int l16,
+                                               int level, int start, bool active, int s,
+                                               const QueryRegs<D>& q)
+{
+    constexpr int LPR = D / 16;
+    const uint32_t b16 = (uint32_t)T >> l16;
+    const uint32_t r = ((uint32_t)T >> level) + ((uint32_t)start >> level);
+    const bool k32 = active && level > l16;
+    const bool k16 = active && level > 0 && level <= l16;
+    const bool kk = active && level == 0;
+    const uint32_t o32 = r * (uint32_t)(4 * D);
+    const uint32_t o16 = b16 * (uint32_t)(4 * D) + (r - b16) * (uint32_t)(2 * D);
+    int4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t slot = 16u * (uint32_t)(j * LPR + s);
+        const uint32_t off = k32 ? o32 + slot : ((k16 && j < 2) ? o16 + slot : slot);
+        v[j] = load16(nbase, off);
+    }
+    const int4 vk = load16(kbase, kk ? (uint32_t)start * (uint32_t)D + 16u * (uint32_t)s
+                                     : 16u * (uint32_t)s);
+    int qh[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        qh[j] = q.qh[j];
+        asm volatile("" : "+v"(qh[j]));
+    }
+    int a32 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        a32 += imul<MUL24>(lo16(qh[2 * j]), v[j].x);
+        a32 += imul<MUL24>(hi16(qh[2 * j]), v[j].y);
+        a32 += imul<MUL24>(lo16(qh[2 * j + 1]), v[j].z);
+        a32 += imul<MUL24>(hi16(qh[2 * j + 1]), v[j].w);
+    }
+    int a16 = 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        a16 = dot2_i16(q.qh[4 * k + 0], v[k].x, a16);
+        a16 = dot2_i16(q.qh[4 * k + 1], v[k].y, a16);
+        a16 = dot2_i16(q.qh[4 * k + 2], v[k].z, a16);
+        a16 = dot2_i16(q.qh[4 * k + 3], v[k].w, a16);
+    }
+    int ak = dot4_i8(q.qp[0], vk.x, 0);
+    ak = dot4_i8(q.qp[1], vk.y, ak);
+    ak = dot4_i8(q.qp[2], vk.z, ak);
+    ak = dot4_i8(q.qp[3], vk.w, ak);
+    const int acc = k32 ? a32 : (k16 ? a16 : (kk ? ak : 0));
+    return group_sum<LPR>(acc);
+}
+
+// The cover roots of [0, ms) (candidate slots L-1-b, an empty key where bit
+// b of ms is clear) and the window positions ms .. t (scores in nsc), with
+// ms = t + 1 - nw, over the threads v < kCoverWaves * 64 of waves 4-7.  With
+// APPEND, position t (whose key row is not stored yet) is left to the
+// predictor's threads (nw - 1 window positions here).
+template <int D, bool MUL24, bool APPEND>
+__device__ __forceinline__ void cover_block(int v, const int32_t* __restrict__ nodes_pair,
+                                            const int8_t* __restrict__ keys_pair, int T, int L,
+                                            int l16, int t, int nw, const QueryRegs<D>& q,
+                                            BlockShared& bs)
+{
+    constexpr int LPR = D / 16, RPG = kWave / LPR, RPC = RPG * kCoverWaves;
+    const int lane = lane_id(), s = lane % LPR, e0 = (v / kWave) * RPG + lane / LPR;
+    const int ms = t + 1 - nw;
+    const int nwin = APPEND ? nw - 1 : nw;
+    gbyte* nbase = uniform_base(nodes_pair);
+    gbyte* kbase = uniform_base(keys_pair);
+    for (int base = 0; base < L + nwin; base += RPC) {
+        const int j = base + e0;
+        const bool cov = j < L;
+        const bool act_cov = cov && ((ms >> j) & 1);
+        const int k = j - L;
+        const bool act_win = !cov && k < nwin;
+        const int level = act_cov ? j : 0;
+        const int start = act_cov ? (ms & ~((2 << j) - 1)) : (act_win ? ms + k : 0);
+        const int sc = score_node_flat<D, MUL24>(nbase, kbase, T, l16, level, start,
+                                                 act_cov || act_win, s, q);
+        if (lane % LPR == 0) {
+            if (cov) bs.sm.cand[L - 1 - j] = act_cov ? make_key(sc, start, j) : 0ull;
+            else if (act_win) bs.nsc[k] = sc;
+        }
+    }
+}
+
+// Left children of two beam entries per row group, when none of the wave's
+// rows is an int32 row: an int16 row (two loads) or a key row (one) per
+// entry, every load of both entries issued before any is used, so a round
+// whose beam needs two block passes waits for memory once.  Loads are masked
+// per lane by the row kind (a lane that loads nothing issues no address).
+// Offsets as in score_row.
+template <int D>
+__device__ __forceinline__ void score_two_rows(gbyte* nbase, gbyte* nbase_hi, gbyte* kbase,
+                                               uint32_t ts0, int cl0, bool x0, uint32_t ts1,
+                                               int cl1, bool x1, int l16, uint32_t o16,
+                                               uint32_t okey, const QueryRegs<D>& q, int& left0,
+                                               int& left1)
+{
+    constexpr int LPR = D / 16;
+    const uint32_t ts[2] = {ts0, ts1};
+    const int cl[2] = {cl0, cl1};
+    const bool ex[2] = {x0, x1};
+    int4 a[2], b[2], c[2];
+    bool k16[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        k16[i] = ex[i] && (uint32_t)(cl[i] - 1) < (uint32_t)l16;
+        const bool kk = ex[i] && cl[i] == 0;
+        const uint32_t off16 = (ts[i] >> (uint32_t)(cl[i] & 31)) * (uint32_t)(2 * D) + o16;
+        const uint32_t offk = ts[i] * (uint32_t)D + okey;
+        a[i] = make_int4(0, 0, 0, 0);
+        b[i] = a[i];
+        c[i] = a[i];
+        if (k16[i]) {
+            a[i] = load16(nbase, off16);
+            b[i] = load16(nbase_hi, off16);
+        }
+        if (kk) c[i] = load16(kbase, offk);
+    }
+    int left[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        int h = dot2_i16_first(q.qh[0], a[i].x);
+        h = dot2_i16(q.qh[1], a[i].y, h);
+        h = dot2_i16(q.qh[2], a[i].z, h);
+        h = dot2_i16(q.qh[3], a[i].w, h);
+        h = dot2_i16(q.qh[4], b[i].x, h);
+        h = dot2_i16(q.qh[5], b[i].y, h);
+        h = dot2_i16(q.qh[6], b[i].z, h);
+        h = dot2_i16(q.qh[7], b[i].w, h);
+        int k = dot4_i8_first(q.qp[0], c[i].x);
+        k = dot4_i8(q.qp[1], c[i].y, k);
+        k = dot4_i8(q.qp[2], c[i].z, k);
+        k = dot4_i8(q.qp[3], c[i].w, k);
+        left[i] = group_sum<LPR>(k16[i] ? h : k);
+    }
+    left0 = left[0];
+    left1 = left[1];
+}
+
+// The children of beam entry i (as in route_query; an empty slot, high word
+// 0, for a node kept as it is); every lane of the row group stores the same
+// two keys.
+__device__ __forceinline__ void write_children(uint64_t* cand, int i, uint64_t key, bool expand,
+                                               int left)
+{
+    const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
+    const int cl = (int)(lo & 31u) - 1;
+    const uint32_t c0hi = expand ? (uint32_t)left ^ 0x80000000u : hi;
+    const uint32_t c1hi = expand ? hi - (uint32_t)left : 0u;
+    const uint32_t c1lo = lo - 1u - (32u << ((uint32_t)cl & 31u));
+    cand[2 * i] = ((uint64_t)c0hi << 32) | (lo - (uint32_t)expand);
+    cand[2 * i + 1] = ((uint64_t)c1hi << 32) | c1lo;
+}
+
+// The beam descent of one decode query from the cover candidates cand[0, L)
+// (written by cover_block) to r routed keys, which end in slots 0 .. r-1 of
+// pos / score in ascending position order.
+template <int D, bool MUL24>
+__device__ void descend_block(const int32_t* __restrict__ nodes_pair,
+                              const int8_t* __restrict__ keys_pair, int T, int L, int l16, int r,
+                              const QueryRegs<D>& q, BlockShared& bs)
 {
     constexpr int LPR = D / 16, RPG = kWave / LPR, RPB = RPG * kDecodeWaves;
     WaveLds& sm = bs.sm;
     const int lane = lane_id(), wv = threadIdx.x / kWave;
     const int s = lane % LPR, e0 = wv * RPG + lane / LPR;
-    const int C = uniform(B < t + 1 ? B : t + 1);
-    const int n = uniform(window < C ? window : C);
-    const int r = C - n;
-    const int m = t + 1 - n;
-
-    for (int base = 0; base < n; base += RPB) {
-        const int k = base + e0;
-        const bool act = k < n;
-        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, l16, 0, m + k, act, s, q);
-        if (act && s == 0) {
-            sm.pos[r + k] = m + k;
-            sm.score[r + k] = sc;
-        }
-    }
-    if (r == 0) {
-        __syncthreads();
-        return C;
-    }
-    for (int base = 0; base < L; base += RPB) {
-        const int b = base + e0;
-        const bool act = b < L && ((m >> b) & 1);
-        const int start = act ? (m & ~((2 << b) - 1)) : 0;
-        const int sc = score_node<D, MUL24>(nodes_pair, keys_pair, T, l16, b, start, act, s, q);
-        if (b < L && s == 0) sm.cand[L - 1 - b] = act ? make_key(sc, start, b) : 0ull;
-    }
-    __syncthreads();
     // the descent's loop invariants (see score_row)
     gbyte* nbase = uniform_base(nodes_pair);
     gbyte* nbase_hi = nbase + 16 * LPR;
@@ -904,26 +1142,30 @@ __device__ int route_query_block(const int32_t* __restrict__ nodes_pair,
         __syncthreads();
         const int nb = uniform(bs.nb);
         if (!uniform(bs.inner)) break;
-        for (int base = 0; base < nb; base += RPB) {
-            const int i = base + e0;
-            const bool valid = i < nb;
-            const uint64_t key = sm.beam[valid ? i : 0];
-            const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
-            const int lv = (int)(lo & 31u);
-            const bool expand = valid && lv > 0;
-            const int cl = lv - 1;
-            const int left = score_row<D, MUL24>(nbase, nbase_hi, kbase, tstart - (lo >> 5), cl, l16,
-                                                 expand, s, o16, okey, q);
-            // children from the parent key, an empty slot (high word 0) for a
-            // node kept as it is (as in route_query); every lane of the row
-            // group stores the same two keys
-            if (valid) {
-                const uint32_t c0hi = expand ? (uint32_t)left ^ 0x80000000u : hi;
-                const uint32_t c1hi = expand ? hi - (uint32_t)left : 0u;
-                const uint32_t c1lo = lo - 1u - (32u << ((uint32_t)cl & 31u));
-                sm.cand[2 * i] = ((uint64_t)c0hi << 32) | (lo - (uint32_t)expand);
-                sm.cand[2 * i + 1] = ((uint64_t)c1hi << 32) | c1lo;
+        for (int base = 0; base < nb; base += 2 * RPB) {
+            // entries i0 = base + e0 and i1 = i0 + RPB of this row group
+            const int i0 = base + e0, i1 = i0 + RPB;
+            const bool v0 = i0 < nb, v1 = i1 < nb;
+            const uint64_t key0 = sm.beam[v0 ? i0 : 0], key1 = sm.beam[v1 ? i1 : 0];
+            const int cl0 = (int)((uint32_t)key0 & 31u) - 1, cl1 = (int)((uint32_t)key1 & 31u) - 1;
+            const bool x0 = v0 && cl0 >= 0, x1 = v1 && cl1 >= 0;
+            const uint32_t ts0 = tstart - ((uint32_t)key0 >> 5), ts1 = tstart - ((uint32_t)key1 >> 5);
+            // the wave's second entries exist; none of its rows is an int32 row
+            const bool second = __ballot(v1) != 0ull;
+            const bool wide = __ballot((x0 && cl0 > l16) || (x1 && cl1 > l16)) != 0ull;
+            int left0, left1 = 0;
+            if (second && !wide) {
+                score_two_rows<D>(nbase, nbase_hi, kbase, ts0, cl0, x0, ts1, cl1, x1, l16, o16,
+                                  okey, q, left0, left1);
+            } else {
+                left0 = score_row<D, MUL24>(nbase, nbase_hi, kbase, ts0, cl0, l16, x0, s, o16,
+                                            okey, q);
+                if (second)
+                    left1 = score_row<D, MUL24>(nbase, nbase_hi, kbase, ts1, cl1, l16, x1, s, o16,
+                                                okey, q);
             }
+            if (v0) write_children(sm.cand, i0, key0, x0, left0);
+            if (v1) write_children(sm.cand, i1, key1, x1, left1);
         }
         ncand = 2 * nb;
         __syncthreads();
@@ -934,8 +1176,6 @@ __device__ int route_query_block(const int32_t* __restrict__ nodes_pair,
         sm.pos[i] = key_start(k);
         sm.score[i] = key_score(k);
     }
-    __syncthreads();
-    return C;
 }
 
 // Softmax weights by wave 0, the value gather shared by every wave, partial
@@ -1016,15 +1256,16 @@ __device__ void attend_block(BlockShared& bs, int C, int T, float scale,
     }
 }
 
-// APPEND: first store the new key and value rows at pos and add the key to
-// the pair's ancestor sums and running sum (append.h, spread over the
-// workgroup's threads),
-// then route and attend; the barrier between the two phases makes the
-// workgroup's global writes visible to its own reads (one CU, workgroup-scope
-// release and acquire).  Only the pair's own rows are touched, so workgroups
-// stay independent.
+// One workgroup per pair: the first phase (budget and append on waves 0-3,
+// cover and window on waves 4-7, see above), then the descent, then the
+// attention.  With APPEND the new key and value rows are stored at pos, the
+// key is added to the pair's ancestor sums (append.h) and the running sum
+// becomes S[pos]; the attention reads the value row at pos after several
+// workgroup barriers, which make the workgroup's global writes visible to its
+// own reads (one CU, workgroup-scope release and acquire).  Only the pair's
+// own rows are touched, so workgroups stay independent.
 template <int D, bool MUL24, bool APPEND>
-__global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_num_sgpr(80))) void k_decode(
+__global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_num_sgpr(80), amdgpu_waves_per_eu(D >= 256 ? 4 : 8))) void k_decode(
     const int8_t* __restrict__ q_new, const int8_t* __restrict__ k_new,
     const float* __restrict__ v_new, int8_t* __restrict__ K, float* __restrict__ V,
     int32_t* __restrict__ nodes, int32_t* __restrict__ prefix,
@@ -1035,29 +1276,72 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_num_sgp
     __shared__ BlockShared bs;
     const uint32_t pair = xcd_logical_block();
     if (pair >= (uint32_t)P) return;   // uniform over the workgroup
-    if constexpr (APPEND) {
-        appendk::append_columns_spread<D, kDecodeWaves * kWave>((int)pair, k_new, v_new, K, V,
-                                                                nodes, prefix, T, L, l16, pos);
-        __syncthreads();
-    }
     const int lane = lane_id(), wv = threadIdx.x / kWave;
     const int s = lane % (D / 16);
     const int8_t* qp = q_new + (size_t)pair * D;
-    QueryRegs<D> q;
-    load_query<D>(qp, s, q);
-    if (wv == 0) {
-        const int B = W ? predict_one<D>(qp, prefix + (size_t)pair * D, W, nc, kpc, max_budget)
-                        : fixed_budget;
-        if (lane == 0) {
-            bs.budget = B;
-            if (budget_out) budget_out[pair] = B;
+    const int8_t* kn = APPEND ? k_new + (size_t)pair * D : nullptr;
+    int32_t* pre = prefix + (size_t)pair * D;
+    const int32_t* nodes_pair = nodes + (size_t)pair * T * D;
+    const int8_t* keys_pair = K + (size_t)pair * T * D;
+    const int t = pos;
+    int nw = window < max_budget ? window : max_budget;
+    nw = nw < t + 1 ? nw : t + 1;
+    if (wv < kPredictWaves) {
+        const int u = threadIdx.x;
+        appendk::SpreadAppend<D, kPredictThreads> app;
+        if constexpr (APPEND) app.load(u, (int)pair, k_new, nodes, T, L, l16, pos);
+        if (W) predict_block<D, APPEND>(u, qp, pre, kn, W, nc, nw, bs);
+        else if (APPEND) own_score<D>(u, qp, kn, nw, bs);
+        if constexpr (APPEND) app.store(u, (int)pair, nodes, T, L, l16, pos);
+    } else {
+        const int v = threadIdx.x - kPredictThreads;
+        // the new key and value rows at pos (stored after the cover's loads)
+        int kw = 0;
+        float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (APPEND && v < D / 4) {
+            kw = reinterpret_cast<const int*>(kn)[v];
+            vv = reinterpret_cast<const float4*>(v_new + (size_t)pair * D)[v];
+        }
+        QueryRegs<D> q;
+        load_query<D>(qp, s, q);
+        cover_block<D, MUL24, APPEND>(v, nodes_pair, keys_pair, T, L, l16, t, nw, q, bs);
+        if (APPEND && v < D / 4) {
+            const size_t row = (size_t)pair * T + pos;
+            reinterpret_cast<int*>(K)[row * (D / 4) + v] = kw;
+            reinterpret_cast<float4*>(V)[row * (D / 4) + v] = vv;
         }
     }
+    // the query in registers for the descent (loaded after the first phase,
+    // whose parts hold enough registers of their own)
+    QueryRegs<D> q;
+    load_query<D>(qp, s, q);
     __syncthreads();
-    const int B = uniform(bs.budget);
-    const int C = route_query_block<D, MUL24>(nodes + (size_t)pair * T * D,
-                                               K + (size_t)pair * T * D, T, L, l16, pos, B,
-                                               window, q, bs);
+    if constexpr (APPEND) {
+        // the running sum becomes S[pos]: the predictor's (left in LDS), or,
+        // without a predictor, formed here
+        if (W) {
+            if (threadIdx.x < D / 4) reinterpret_cast<int4*>(pre)[threadIdx.x] = bs.snew[threadIdx.x];
+        } else if (threadIdx.x < D / 4) {
+            const int kw = reinterpret_cast<const int*>(kn)[threadIdx.x];
+            int4* p4 = reinterpret_cast<int4*>(pre) + threadIdx.x;
+            const int4 p = *p4;
+            *p4 = make_int4(p.x + sbyte(kw, 0), p.y + sbyte(kw, 1), p.z + sbyte(kw, 2),
+                            p.w + sbyte(kw, 3));
+        }
+    }
+    const int B = uniform(W ? budget_from_best(bs, kpc, max_budget) : fixed_budget);
+    if (threadIdx.x == 0 && budget_out) budget_out[pair] = B;
+    const int C = uniform(B < t + 1 ? B : t + 1);
+    const int n = uniform(window < C ? window : C);
+    const int r = C - n;
+    const int m = t + 1 - n;
+    // neighbours m .. t are the last n window positions; they go to slots r..
+    if ((int)threadIdx.x < n) {
+        bs.sm.pos[r + threadIdx.x] = m + (int)threadIdx.x;
+        bs.sm.score[r + threadIdx.x] = bs.nsc[nw - n + (int)threadIdx.x];
+    }
+    if (r > 0) descend_block<D, MUL24>(nodes_pair, keys_pair, T, L, l16, r, q, bs);
+    __syncthreads();
     if (wv == 0) write_selection(bs.sm, C, max_budget, idx + (size_t)pair * max_budget, count + pair);
     attend_block<D>(bs, C, T, scale, V + (size_t)pair * T * D, O + (size_t)pair * D);
 }
