@@ -142,20 +142,38 @@ def bytes_per_query(stats, cfg, budget_read=True):
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 
-def dense_summary(w, dense_ms, step_ms):
+# The dense kernel's P.V split: P and V each as a bf16 head plus a bf16 tail
+# (x = hi + lo to within 2^-18 |x|), hi.hi + lo.hi + hi.lo summed in fp32:
+# each output within 3 * 2^-18 * max|V| of the fp32 product.
+DENSE_PV_REL_BOUND = 3 * 2.0 ** -18
+PARITY_ATOL = 1e-4
+
+
+def dense_summary(w, dense_ms, step_ms, max_abs_v=None):
     """The dense causal baseline's time and its matrix-core roofline: per
     (query, past key) pair 2d int8 ops for the score and, for P.V, three bf16
     products of 2d flops each (heads and tails of P and V), against the bf16
-    dense peak (the int8 score work is a thirtieth of it and left out)."""
+    dense peak (the int8 score work is a thirtieth of it and left out).  The
+    precision entry states the split's error bound for this workload's
+    values against the routed path's fp32 products."""
     pairs = w.B * w.H * w.T * (w.T + 1) / 2
     bf16_flops = 3 * 2 * w.d * pairs
     achieved = bf16_flops / (dense_ms * 1e-3) / 1e12
-    return {"kernel": "alhr_dense_attend (causal, int8 MFMA scores, P.V as three bf16 MFMA "
-                      "products, fp32-accurate)",
-            "ms": dense_ms, "routed_step_speedup": dense_ms / step_ms,
-            "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
-                         "fp32_equivalent_tflops": achieved / 3}}
+    out = {"kernel": "alhr_dense_attend (causal, int8 MFMA scores, P.V as three bf16 MFMA "
+                     "products)",
+           "ms": dense_ms, "routed_step_speedup": dense_ms / step_ms,
+           "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
+                        "fp32_equivalent_tflops": achieved / 3}}
+    if max_abs_v is not None:
+        bound = DENSE_PV_REL_BOUND * max_abs_v
+        out["precision"] = {
+            "pv_abs_error_bound": bound, "max_abs_v": max_abs_v, "parity_atol": PARITY_ATOL,
+            "within_parity_atol": bool(bound <= PARITY_ATOL),
+            "max_abs_v_for_atol": PARITY_ATOL / DENSE_PV_REL_BOUND,
+            "note": "P.V from bf16 heads and tails: each output within 3*2^-18*max|V| of fp32; "
+                    "the routed path multiplies in fp32 (no bound on V)"}
+    return out
 
 
 def host_cores():
@@ -440,7 +458,8 @@ def bench_prefill(args, torch, dev):
                              "graph of alhr_route_attend"},
         "roofline": route_roofline(kern["route_attend_ms"], queries, bpl, issue, traffic),
         "kernels_ms": kern,
-        "dense_baseline": None if dense_ms is None else dense_summary(w, dense_ms, ms_step),
+        "dense_baseline": None if dense_ms is None else dense_summary(
+            w, dense_ms, ms_step, float(np.abs(V).max())),
         "splitter": splitter,
         "diagnostics": {"mean_budget": float(bud.mean()), "mean_keys_per_query": float(cnt.mean()),
                         "budget_histogram": {int(v): int(c) for v, c in

@@ -95,6 +95,12 @@ def test_dense_roofline_by_hand():
     assert out["roofline"]["achieved"] == pytest.approx(flops / 1e-3 / 1e12)
     assert out["roofline"]["frac"] == pytest.approx(out["roofline"]["achieved"] / 2500.0)
     assert out["routed_step_speedup"] == 2.0
+    assert "precision" not in out
+    # 3 * 2^-18 * max|V|: 1.14e-5 at |V| = 1, beyond the 1e-4 bar above |V| = 8.74
+    prec = bench.dense_summary(W(), 1.0, 0.5, max_abs_v=1.0)["precision"]
+    assert prec["pv_abs_error_bound"] == pytest.approx(3 * 2.0 ** -18)
+    assert prec["within_parity_atol"] and prec["max_abs_v_for_atol"] == pytest.approx(8.738, rel=1e-3)
+    assert not bench.dense_summary(W(), 1.0, 0.5, max_abs_v=9.0)["precision"]["within_parity_atol"]
 
 
 def test_issue_file_is_read_only_for_the_matching_source(tmp_path, monkeypatch):
