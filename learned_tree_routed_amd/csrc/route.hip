@@ -69,7 +69,6 @@ __device__ __forceinline__ uint64_t make_key(int score, int start, int level)
 }
 __device__ __forceinline__ int key_score(uint64_t k) { return (int)((uint32_t)(k >> 32) ^ 0x80000000u); }
 __device__ __forceinline__ int key_start(uint64_t k) { return 0xFFFFF - (int)((uint32_t)k >> 5); }
-__device__ __forceinline__ int key_level(uint64_t k) { return (int)((uint32_t)k & 31u); }
 
 // ---- the query in registers, in the two column layouts used for scoring ---
 // Lane s of a row group (LPR = d / 16 lanes per row) holds the columns of the
@@ -747,7 +746,8 @@ __device__ __forceinline__ void route_one(const RouteArgs& a, uint64_t gw, WaveL
 // workgroups go to consecutive XCDs instead: every XCD takes an equal share of
 // every pair, at the price of each L2 holding every pair's rows in turn (the
 // openai-hub article, section "次二次复杂度成立，需要满足三个前提", on GPU
-// utilisation under divergent tree search).
+// utilisation under divergent tree search).  A fixed budget is the same for
+// every pair, so there the contiguous ranges keep their L2 locality.
 constexpr int kPairsPerXcd = 8;
 
 template <int D, bool MUL24, bool ATTEND, bool STATS>
@@ -1376,7 +1376,7 @@ hipError_t route_d(const Shape& s, const int8_t* Q, const int8_t* K, const float
     for (uint64_t q0 = 0; q0 < total; q0 += kQueriesPerLaunch) {
         a.q0 = q0;
         a.nq = total - q0 < kQueriesPerLaunch ? total - q0 : kQueriesPerLaunch;
-        a.interleave = a.nq < (uint64_t)kXcds * kPairsPerXcd * s.T;
+        a.interleave = budget != nullptr && a.nq < (uint64_t)kXcds * kPairsPerXcd * s.T;
         hipError_t e;
         if (stats) e = launch_one<D, MUL24, false, true>(a, st);
         else if (O) e = launch_one<D, MUL24, true, false>(a, st);
