@@ -6,8 +6,8 @@
 A step is one pass of the whole prefill path over one batch: tree build and
 budget prediction (alhr_prepare: the two share their launches), then the
 fused route + attend kernel, i.e. the kernels alhr_forward launches, issued
-as its two ABI calls, each replayed from a HIP graph, with HIP events on the
-launch stream around each replay.  Untimed auxiliary measurements (the
+as its two ABI calls back to back, with HIP events on the launch stream
+around each call.  Untimed auxiliary measurements (the
 routing's load counts, the dense baseline, the splitter) run first.  Inputs
 are synthetic and resident in HBM before the timed region.  Prints one JSON
 line:
@@ -404,30 +404,36 @@ def bench_prefill(args, torch, dev):
     # timed on its own: it precedes the tree path and is not part of a step
     splitter = bench_splitter(alhr, torch, dev, w)
 
-    # The timed steps: each one replays two HIP graphs, the preparation
-    # (tree + budgets, alhr_prepare) and the fused route + attend
-    # (alhr_route_attend), with HIP events on the launch stream (torch's
-    # current stream, on which the binding launches and the graphs replay)
-    # around each, so the route kernel's duration is measured in the timed
-    # region itself.
-    g_prep = capture_step(torch, lambda: alhr.alhr_prepare(cfg, q, k, wb, nodes, bb, wsb))
-    g_route = capture_step(torch, lambda: alhr.alhr_route_attend(cfg, q, k, v, nodes, bb, fixed,
-                                                                 idx, count, O))
+    # The timed steps: each one is the two calls, the preparation (tree +
+    # budgets, alhr_prepare) and the fused route + attend (alhr_route_attend),
+    # launched directly, with HIP events on the launch stream (torch's current
+    # stream, on which the binding launches) before, between and after them,
+    # so the route kernel's duration is measured in the timed region itself.
+    # A step takes about half a millisecond of GPU time and its three launches
+    # a few tens of microseconds of host time, so the host stays ahead and the
+    # kernels run back to back (replaying each call as a HIP graph instead
+    # added about 8 microseconds per graph on this platform).
+    def prep():
+        alhr.alhr_prepare(cfg, q, k, wb, nodes, bb, wsb)
+
+    def route():
+        alhr.alhr_route_attend(cfg, q, k, v, nodes, bb, fixed, idx, count, O)
+
     # untimed settle phase: the GPU reaches its steady clocks after a few tens
     # of milliseconds of this kernel (with 5 steps only, the timed route
     # launches ran 5% slower), then the W warm-up steps
     for _ in range(SETTLE_STEPS + args.warmup):
-        g_prep.replay()
-        g_route.replay()
+        prep()
+        route()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e in events:
         e[0].record()
-        g_prep.replay()
+        prep()
         e[1].record()
-        g_route.replay()
+        route()
         e[2].record()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
@@ -454,8 +460,8 @@ def bench_prefill(args, torch, dev):
                    "window": cfg.window, "max_budget": cfg.max_budget,
                    "budget": ("fixed %d" % fixed) if fixed else "int8 predictor, 32 classes x 3",
                    "queries_per_step": queries,
-                   "launch": "per step: HIP graph of alhr_prepare (build + predict), then HIP "
-                             "graph of alhr_route_attend"},
+                   "launch": "per step: alhr_prepare (build + predict), then "
+                             "alhr_route_attend, launched back to back"},
         "roofline": route_roofline(kern["route_attend_ms"], queries, bpl, issue, traffic),
         "kernels_ms": kern,
         "dense_baseline": None if dense_ms is None else dense_summary(
@@ -710,7 +716,8 @@ def bench_sweep(args, torch, dev):
             step(e)
         torch.cuda.synchronize()
         kms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-        # step time from graph replays of the same calls, as in the main bench
+        # step time from graph replays of the same calls (at the short lengths
+        # a step takes about as long as the host needs to issue its launches)
         graph = capture_step(torch, lambda: step_calls(alhr, cfg, Q, K, V, Wt, nodes, bud, ws, 0,
                                                        idx, cnt, O))
         for _ in range(max(1, args.warmup)):
