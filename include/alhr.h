@@ -256,10 +256,12 @@ alhr_status alhr_decode_step(const alhr_config *cfg, int32_t pos,
 /* Append and decode step in one launch: alhr_append(pos, k_new, v_new)
  * followed by alhr_decode_step(pos, q_new), with the same arguments, layouts,
  * results and error codes (prefix is required).  Each (batch, head) pair's
- * workgroup appends its own key and value rows before it routes, so no
- * pair waits for another; this saves the second launch of every token step
- * (openai-hub article "ALHR把注意力变成树搜索", section "ALHR是什么": one new
- * token per step). */
+ * workgroup appends its own key and value rows while it predicts and routes:
+ * the route reads only subtrees of [0, pos + 1 - n) and the key rows below
+ * pos (the new key itself from k_new), none of which the append changes, and
+ * the predictor forms the new running sum itself; so no pair waits for another, and this saves the
+ * second launch of every token step (openai-hub article
+ * "ALHR把注意力变成树搜索", section "ALHR是什么": one new token per step). */
 alhr_status alhr_append_decode(const alhr_config *cfg, int32_t pos,
                                const int8_t *k_new, const float *v_new,
                                const int8_t *q_new, int8_t *K, float *V,
