@@ -256,3 +256,49 @@ def test_decode_from_empty_cache_every_step(torch_dev, T, d, fixed, fused):
         np.testing.assert_array_equal(decode_tree(nodes[b, h].cpu().numpy(), l16)[1:],
                                       ref_nodes[1:])
         np.testing.assert_array_equal(prefix[b, h].cpu().numpy(), ref_pre)
+
+
+WINDOW_CASES = [
+    # T, d, window, fixed budget (0 = predictor), max_budget
+    (256, 64, 40, 16, 96),       # window wider than the budget: n = C, no cover
+    (256, 32, 1, 0, 96),         # a window of one key (the own key)
+    (256, 128, 7, 0, 96),        # an odd window
+    (128, 64, 40, 0, 32),        # window wider than max_budget (the window is cut to it)
+    (128, 16, 1 << 20, 0, 40),   # a window far past T
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["two_launches", "fused"])
+@pytest.mark.parametrize("T,d,window,fixed,mb", WINDOW_CASES,
+                         ids=["T%d_d%d_w%d_f%d_mb%d" % c for c in WINDOW_CASES])
+def test_decode_window_edges_every_step(torch_dev, T, d, window, fixed, mb, fused):
+    """Decoding from an empty cache with windows other than 4: the decode
+    kernel scores the window before the budget is known, for the widest n the
+    query can have (at most window, max_budget and t + 1 keys), and places
+    the last n of them; with a fixed budget and the fused append the own key's
+    score comes from the new key row.  Every step equals the oracle's replay."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    w = Workload("decode_window", 9, 1, 2, T, d, "clustered", fixed_budget=fixed, window=window,
+                 max_budget=mb)
+    cfg = w.config()
+    Q, K, V, W = host_inputs(w)
+    say("decode window edges: B1 H2 T%d d%d window %d fixed %d max_budget %d"
+        % (T, d, window, fixed, mb))
+    Kd = torch.zeros((1, 2, T, d), dtype=torch.int8, device=dev)
+    Vd = torch.zeros((1, 2, T, d), dtype=torch.float32, device=dev)
+    nodes = alhr.alhr_build_tree(cfg, Kd)
+    prefix = alhr.alhr_prefix_from_tree(cfg, 0, Kd, nodes)
+    Wd = None if W is None else torch.from_numpy(W).to(dev)
+    Kh, Vh, Qh = (torch.from_numpy(x).to(dev) for x in (K, V, Q))
+    pairs = [(0, 0), (0, 1)]
+    got = run_decode(torch, dev, w, cfg, Kd, Vd, nodes, prefix, Wd, 0, T, pairs,
+                     lambda p: Qh[:, :, p].contiguous(), lambda p: Kh[:, :, p].contiguous(),
+                     lambda p: Vh[:, :, p].contiguous(), fused=fused)
+    l16 = alhr.alhr_tree_int16_levels(cfg)
+    for (b, h) in pairs:
+        ref, ref_nodes, ref_pre = decode_oracle_pair(w, b, h, 0, T, K[b, h], Q[b, h], W, cfg)
+        compare(got[(b, h)], ref)
+        np.testing.assert_array_equal(decode_tree(nodes[b, h].cpu().numpy(), l16)[1:],
+                                      ref_nodes[1:])
+        np.testing.assert_array_equal(prefix[b, h].cpu().numpy(), ref_pre)
