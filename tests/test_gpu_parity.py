@@ -127,6 +127,37 @@ def test_full_size_sampled(torch_dev, name):
     np.testing.assert_array_equal(last, np.broadcast_to(t, last.shape))
 
 
+@pytest.mark.parametrize("name", ["t4k", "t16k"])
+def test_full_size_every_query(torch_dev, name):
+    """Every query of the full workload (131072 at t4k and at t16k), launched
+    as the benchmark times it (alhr_prepare, then alhr_route_attend with the
+    predictor's budgets), against the oracle run on every query of every
+    pair: budgets, index sets and counts bit-exact, outputs within 1e-4."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    w = WORKLOADS[name]
+    Q, K, V, W = host_inputs(w)
+    cfg = w.config()
+    q, k, v, wt = to_dev(torch, dev, Q, K, V, W)
+    say("alhr_prepare + alhr_route_attend, every query of", name)
+    nodes, budget = alhr.alhr_prepare(cfg, q, k, wt)
+    idx, count, O = alhr.alhr_route_attend(cfg, q, k, v, nodes, budget)
+    torch.cuda.synchronize()
+    bud, idx, count, O = (t.cpu().numpy() for t in (budget, idx, count, O))
+    worst = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            ref = oracle.pair_forward(Q[b, h], K[b, h], V[b, h], W=W, window=cfg.window,
+                                      keys_per_class=cfg.keys_per_class,
+                                      max_budget=cfg.max_budget, scale=cfg.scale)
+            np.testing.assert_array_equal(bud[b, h], ref["budget"], err_msg="(%d, %d)" % (b, h))
+            np.testing.assert_array_equal(count[b, h], ref["count"], err_msg="(%d, %d)" % (b, h))
+            np.testing.assert_array_equal(idx[b, h], ref["idx"], err_msg="(%d, %d)" % (b, h))
+            worst = max(worst, float(np.abs(O[b, h] - ref["O"]).max()))
+    assert worst <= ATOL, worst
+    say("  max |O - oracle| over every query: %.3g" % worst)
+
+
 # ------------------------------------------------------- entry-point paths --
 def test_unfused_path_equals_fused(torch_dev):
     import learned_tree_routed_amd as alhr
