@@ -950,7 +950,7 @@ __device__ __forceinline__ int budget_from_best(const BlockShared& bs, int kpc, 
 // q . node with every kind of row loaded at once and no branch: four 16-byte
 // loads from the tree table (an int32 row uses all four, an int16 row the
 // first two) and one from the key rows.  Slots a node does not use read row
-// 0, which is allocated and never used.  The first phase's rows are of mixed kinds (cover roots at
+// 0 of their table (allocated; its value is discarded).  The first phase's rows are of mixed kinds (cover roots at
 // every level, window keys); this way they cost one memory round trip, not
 // one per kind.  Inactive lanes give 0.
 template <int D, bool MUL24>
