@@ -425,6 +425,52 @@ def test_route_d64_two_cover_passes_at_2_17(torch_dev):
         assert err <= ATOL, (h, err)
 
 
+def random_config(i):
+    """The i-th seeded random small configuration: shapes, window, budget
+    mode and the magnitude of the int8 queries and keys (which sets how many
+    tree levels are stored as int16)."""
+    rng = np.random.default_rng(9000 + i)
+    d = int(rng.choice([16, 32, 64, 128, 256]))
+    a = int(rng.choice([1, 3, 8, 31, 127]))
+    T = 1 << int(rng.integers(1, 10 if a == 127 else 11))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    window = int(rng.integers(1, 10))
+    max_budget = int(rng.integers(3, 129))
+    if rng.random() < 0.5:
+        mode = dict(fixed=int(rng.integers(1, max_budget + 1)), n_classes=32, kpc=3)
+    else:
+        mode = dict(fixed=0, n_classes=int(rng.integers(1, 33)), kpc=int(rng.integers(1, 5)))
+    return rng, dict(B=B, H=H, T=T, d=d, a=a, window=window, max_budget=max_budget, **mode)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_configs_every_query(torch_dev, i):
+    """Seeded random small configurations (T = 2 .. 1024, d = 16 .. 256,
+    windows 1 .. 9, fixed or predicted budgets with 1 .. 32 classes of 1 .. 4
+    keys, budgets up to 128, |Q|, |K| up to 1 .. 127): the tree, budgets,
+    index sets and counts bit-exact and the outputs within 1e-4 of the oracle
+    on every query of every pair."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    rng, c = random_config(i)
+    B, H, T, d, a = c["B"], c["H"], c["T"], c["d"], c["a"]
+    Q = rng.integers(-a, a + 1, size=(B, H, T, d)).astype(np.int8)
+    K = rng.integers(-a, a + 1, size=(B, H, T, d)).astype(np.int8)
+    V = rng.standard_normal(size=(B, H, T, d)).astype(np.float32)
+    W = None if c["fixed"] else rng.integers(-4, 5, size=(c["n_classes"], 2 * d)).astype(np.int8)
+    cfg = alhr.Config(batch=B, heads=H, T=T, d=d, window=c["window"], n_classes=c["n_classes"],
+                      keys_per_class=c["kpc"], max_budget=c["max_budget"], kmax=a, qmax=a, wmax=4)
+    w = Workload("random%d" % i, 0, B, H, T, d, "uniform", fixed_budget=c["fixed"],
+                 window=c["window"], n_classes=c["n_classes"], keys_per_class=c["kpc"],
+                 max_budget=c["max_budget"])
+    say("random config", i, c)
+    out = run_forward(torch, dev, w, Q, K, V, W, cfg=cfg)
+    for b in range(B):
+        for h in range(H):
+            check_nodes(out["nodes"], K, b, h, cfg)
+            check_pair(w, cfg, Q, K, V, W, out, b, h)
+
+
 # ---------------------------------------------------------------- edges ---
 EDGE_CASES = [
     # name, T, d, window, fixed budget (0 = predictor), max_budget, kind
