@@ -302,3 +302,60 @@ def test_decode_window_edges_every_step(torch_dev, T, d, window, fixed, mb, fuse
         np.testing.assert_array_equal(decode_tree(nodes[b, h].cpu().numpy(), l16)[1:],
                                       ref_nodes[1:])
         np.testing.assert_array_equal(prefix[b, h].cpu().numpy(), ref_pre)
+
+
+
+def random_decode_config(i):
+    rng = np.random.default_rng(7000 + i)
+    d = int(rng.choice([16, 32, 64, 128, 256]))
+    a = int(rng.choice([1, 4, 9, 31, 127]))
+    T = 1 << int(rng.integers(1, 9))
+    window = int(rng.integers(1, 10))
+    max_budget = int(rng.integers(3, 129))
+    if rng.random() < 0.4:
+        mode = dict(fixed=int(rng.integers(1, max_budget + 1)), n_classes=32, kpc=3)
+    else:
+        mode = dict(fixed=0, n_classes=int(rng.integers(1, 33)), kpc=int(rng.integers(1, 5)))
+    return rng, dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 3)), T=T, d=d, a=a,
+                     window=window, max_budget=max_budget, **mode)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["two_launches", "fused"])
+@pytest.mark.parametrize("i", range(8))
+def test_decode_random_configs_every_step(torch_dev, i, fused):
+    """Seeded random small decode configurations (T = 2 .. 256, d = 16 .. 256,
+    windows 1 .. 9, fixed or predicted budgets, |Q|, |K| up to 127), decoded
+    from an empty cache through every position: every step's budget, index
+    set, count and output, and the final tree and running sum, equal the
+    oracle's replay."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    rng, c = random_decode_config(i)
+    B, H, T, d, a = c["B"], c["H"], c["T"], c["d"], c["a"]
+    w = Workload("decode_random%d" % i, 20 + i, B, H, T, d, "uniform", fixed_budget=c["fixed"],
+                 window=c["window"], n_classes=c["n_classes"], keys_per_class=c["kpc"],
+                 max_budget=c["max_budget"])
+    cfg = alhr.Config(batch=B, heads=H, T=T, d=d, window=c["window"], n_classes=c["n_classes"],
+                      keys_per_class=c["kpc"], max_budget=c["max_budget"], kmax=a, qmax=a, wmax=4)
+    Q = rng.integers(-a, a + 1, size=(B, H, T, d)).astype(np.int8)
+    K = rng.integers(-a, a + 1, size=(B, H, T, d)).astype(np.int8)
+    V = synth.values(w.seed, B, H, d, 0, T)     # the rows the oracle replay draws
+    W = None if c["fixed"] else rng.integers(-4, 5, size=(c["n_classes"], 2 * d)).astype(np.int8)
+    say("decode random config", i, "fused" if fused else "two launches", c)
+    Kd = torch.zeros((B, H, T, d), dtype=torch.int8, device=dev)
+    Vd = torch.zeros((B, H, T, d), dtype=torch.float32, device=dev)
+    nodes = alhr.alhr_build_tree(cfg, Kd)
+    prefix = alhr.alhr_prefix_from_tree(cfg, 0, Kd, nodes)
+    Wd = None if W is None else torch.from_numpy(W).to(dev)
+    Kh, Vh, Qh = (torch.from_numpy(x).to(dev) for x in (K, V, Q))
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    got = run_decode(torch, dev, w, cfg, Kd, Vd, nodes, prefix, Wd, 0, T, pairs,
+                     lambda p: Qh[:, :, p].contiguous(), lambda p: Kh[:, :, p].contiguous(),
+                     lambda p: Vh[:, :, p].contiguous(), fused=fused)
+    l16 = alhr.alhr_tree_int16_levels(cfg)
+    for (b, h) in pairs:
+        ref, ref_nodes, ref_pre = decode_oracle_pair(w, b, h, 0, T, K[b, h], Q[b, h], W, cfg)
+        compare(got[(b, h)], ref)
+        np.testing.assert_array_equal(decode_tree(nodes[b, h].cpu().numpy(), l16)[1:],
+                                      ref_nodes[1:])
+        np.testing.assert_array_equal(prefix[b, h].cpu().numpy(), ref_pre)
