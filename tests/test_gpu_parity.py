@@ -601,6 +601,33 @@ def test_dense_attention_every_query(torch_dev, T, d):
             assert err <= ATOL, "pair (%d, %d): max |O - oracle| = %g" % (b, h, err)
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_dense_attention_random_configs(torch_dev, i):
+    """Seeded random shapes for the dense baseline (T = 4 .. 1024, d = 32 ..
+    256, 1 .. 3 pairs, |Q|, |K| up to 127, N(0, 1) values): every query
+    within 1e-4 of the oracle's attention over all past keys."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    rng = np.random.default_rng(6000 + i)
+    d = int(rng.choice([32, 64, 128, 256]))
+    T = 1 << int(rng.integers(2, 11))
+    a = int(rng.choice([1, 4, 31, 127]))
+    B, H = 1, int(rng.integers(1, 4))
+    Q = rng.integers(-a, a + 1, size=(B, H, T, d)).astype(np.int8)
+    K = rng.integers(-a, a + 1, size=(B, H, T, d)).astype(np.int8)
+    V = rng.standard_normal(size=(B, H, T, d)).astype(np.float32)
+    cfg = alhr.Config(batch=B, heads=H, T=T, d=d, kmax=a, qmax=a)
+    q, k, v = to_dev(torch, dev, Q, K, V)
+    say("alhr_dense_attend random config", i, "H%d T%d d%d |q|,|k| <= %d" % (H, T, d, a))
+    O = alhr.alhr_dense_attend(cfg, q, k, v)
+    torch.cuda.synchronize()
+    O = O.cpu().numpy()
+    for h in range(H):
+        ref = dense_oracle_rows(Q[0, h], K[0, h], V[0, h], cfg.scale, range(T))
+        err = np.abs(O[0, h] - ref).max()
+        assert err <= ATOL, "head %d: max |O - oracle| = %g" % (h, err)
+
+
 def test_dense_attention_full_size_sampled(torch_dev):
     import learned_tree_routed_amd as alhr
     torch, dev = torch_dev

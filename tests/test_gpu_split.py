@@ -69,6 +69,33 @@ def test_split_small_every_output(torch_dev, case):
     assert np.abs(q.astype(int)).max() <= qc and np.abs(k.astype(int)).max() <= kc
 
 
+def random_split_case(i):
+    rng = np.random.default_rng(5000 + i)
+    d = int(rng.choice([16, 32, 64, 128, 256]))
+    return (int(rng.integers(1, 4)), int(rng.integers(1, 9)), int(rng.integers(1, 301)), d,
+            16 * int(rng.integers(1, 129)), int(rng.integers(0, 13)), int(rng.integers(1, 128)),
+            int(rng.integers(1, 128)), int(rng.choice([1, 8, 31, 127])))
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_split_random_shapes_every_output(torch_dev, i):
+    """Seeded random shapes (1 .. 3 sequences of 1 .. 300 tokens, 1 .. 8 heads,
+    d = 16 .. 256, d_model a multiple of 16 up to 2048, shifts 0 .. 12, clamps
+    1 .. 127, inputs up to the full int8 range): every output bit-exact."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    batch, heads, T, d, dm, shift, qc, kc, hi = random_split_case(i)
+    lo = -hi - (hi == 127)
+    X = synth.split_inputs(40 + i, batch, dm, 0, T, lo, hi)
+    W = synth.split_weights(40 + i, heads, d, dm, lo, hi)
+    s = alhr.SplitConfig(batch=batch, heads=heads, T=T, d=d, d_model=dm, shift=shift,
+                         qclamp=qc, kclamp=kc)
+    q, k = run_split(torch, dev, s, X, W)
+    rq, rk = oracle.split_qk(X, W, heads, d, shift, qc, kc)
+    np.testing.assert_array_equal(q, rq)
+    np.testing.assert_array_equal(k, rk)
+
+
 def test_split_full_size_sampled_tokens(torch_dev):
     """16384 tokens x d_model 512 -> 8 heads x d 64 (the bench's shapes):
     512 sampled tokens against the oracle, plus whole-output invariants."""
