@@ -881,8 +881,13 @@ def main():
         # the decode workload (the HBM-bound case) in the same line, after the
         # timed prefill steps
         torch.cuda.empty_cache()
-        out["decode"] = decode_measure(torch, dev, args.decode_steps, 1,
-                                       with_cpu=not args.no_cpu_baseline)
+        try:
+            out["decode"] = decode_measure(torch, dev, args.decode_steps, 1,
+                                           with_cpu=not args.no_cpu_baseline)
+        except RuntimeError as e:   # e.g. less free device memory than its 144 GiB cache
+            # the headline line is still printed; the decode entry says why it is missing
+            out["decode"] = {"error": "%s: %s" % (type(e).__name__, str(e)[:300])}
+            torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 
