@@ -359,3 +359,71 @@ def test_decode_random_configs_every_step(torch_dev, i, fused):
         np.testing.assert_array_equal(decode_tree(nodes[b, h].cpu().numpy(), l16)[1:],
                                       ref_nodes[1:])
         np.testing.assert_array_equal(prefix[b, h].cpu().numpy(), ref_pre)
+
+
+
+def test_decode_graph_replays_match_eager(torch_dev):
+    """The decode loop as the benchmark runs it: fused append + decode launches
+    captured in one HIP graph.  Each replay (from a rebuilt cache, with eager
+    work between replays) gives exactly the eager loop's outputs, tree and
+    running sum."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    T, d, steps = 1024, 128, 8
+    n0 = T - steps
+    w = Workload("decode_graph", 11, 2, 2, T, d, "clustered")
+    cfg = w.config()
+    Q, K, V, W = host_inputs(w)
+    Kh, Vh, Qh = (torch.from_numpy(x).to(dev) for x in (K, V, Q))
+    Wd = torch.from_numpy(W).to(dev)
+    Kd = torch.zeros((2, 2, T, d), dtype=torch.int8, device=dev)
+    Vd = torch.zeros((2, 2, T, d), dtype=torch.float32, device=dev)
+    nodes = torch.empty((2, 2, T, d), dtype=torch.int32, device=dev)
+    prefix = torch.empty((2, 2, d), dtype=torch.int32, device=dev)
+    ks = [Kh[:, :, n0 + s].contiguous() for s in range(steps)]
+    vs = [Vh[:, :, n0 + s].contiguous() for s in range(steps)]
+    qs = [Qh[:, :, n0 + s].contiguous() for s in range(steps)]
+    outs = [(torch.empty((2, 2), dtype=torch.int32, device=dev),
+             torch.empty((2, 2, cfg.max_budget), dtype=torch.int32, device=dev),
+             torch.empty((2, 2), dtype=torch.int32, device=dev),
+             torch.empty((2, 2, d), dtype=torch.float32, device=dev)) for _ in range(steps)]
+
+    def reset():
+        Kd.zero_()
+        Vd.zero_()
+        Kd[:, :, :n0] = Kh[:, :, :n0]
+        Vd[:, :, :n0] = Vh[:, :, :n0]
+        alhr.alhr_build_tree(cfg, Kd, nodes)
+        alhr.alhr_prefix_from_tree(cfg, n0, Kd, nodes, prefix)
+
+    def loop():
+        for s_ in range(steps):
+            bud, idx, cnt, O = outs[s_]
+            alhr.alhr_append_decode(cfg, n0 + s_, ks[s_], vs[s_], qs[s_], Kd, Vd, nodes, prefix,
+                                    Wd, 0, bud, idx, cnt, O)
+
+    say("decode graph: eager loop, B2 H2 T%d d%d, %d steps" % (T, d, steps))
+    reset()
+    loop()
+    torch.cuda.synchronize()
+    ref = [tuple(t.clone() for t in o) for o in outs]
+    ref_nodes, ref_prefix = nodes.clone(), prefix.clone()
+    reset()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        loop()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            for t in o:
+                t.zero_()
+        reset()
+        torch.cuda.synchronize()
+        say("decode graph replay", rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            for x, y in zip(a, b):
+                assert torch.equal(x, y)
+        assert torch.equal(nodes, ref_nodes) and torch.equal(prefix, ref_prefix)

@@ -288,6 +288,38 @@ def test_repeat_runs_are_bit_identical(torch_dev):
         assert torch.equal(a0, a1)
 
 
+def test_two_streams_at_once(torch_dev):
+    """Two alhr_forward calls on two streams at the same time, each with its
+    own outputs and workspace (the library keeps no state between calls): both
+    equal a call alone on the default stream."""
+    import learned_tree_routed_amd as alhr
+    torch, dev = torch_dev
+    w = WORKLOADS["t1k"]
+    Q, K, V, W = host_inputs(w, B=2, H=4)
+    cfg = w.config(batch=2, heads=4)
+    q, k, v, wt = to_dev(torch, dev, Q, K, V, W)
+    say("alhr_forward on two streams at once, t1k B2 H4")
+    alone = alhr.alhr_forward(cfg, q, k, v, wt)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]   # default priority
+    outs = []
+    for st in streams:
+        with torch.cuda.stream(st):
+            outs.append(alhr.alhr_forward(cfg, q, k, v, wt))
+    torch.cuda.synchronize()
+    l16 = alhr.alhr_tree_int16_levels(cfg)
+    ref_nodes = alone["nodes"].cpu().numpy()
+    for out in outs:
+        for key in ("budget", "idx", "count", "O"):
+            assert torch.equal(out[key], alone[key]), key
+        # the stored rows (the tail of a compact table is never written)
+        got = out["nodes"].cpu().numpy()
+        for b in range(2):
+            for h in range(4):
+                np.testing.assert_array_equal(decode_tree(got[b, h], l16)[1:],
+                                              decode_tree(ref_nodes[b, h], l16)[1:])
+
+
 def test_launch_geometry_does_not_change_results(torch_dev):
     """The same pairs computed by different waves, blocks and XCDs: alone in a
     B1 H8 launch (fewer than 8 pairs per XCD: queries dealt to the XCDs in
