@@ -282,7 +282,7 @@ def bench_splitter(alhr, torch, dev, w, reps=20):
     ops = 2 * M * N * dm
     nbytes = M * dm + N * dm + M * N
     tops = ops / (ms * 1e-3) / 1e12
-    return {"kernel": "k_split (int8 MFMA 32x32x32, 128x128 tiles)",
+    return {"kernel": "k_split (int8 MFMA 32x32x32, 128x256 tiles)",
             "shape": {"tokens": M, "d_model": dm, "outputs": N},
             "ms": ms, "ops_per_launch": ops, "bytes_per_launch": nbytes,
             "roofline": {"bound": "mfma", "achieved": tops, "peak": INT8_MFMA_PEAK_TOPS,

@@ -6,8 +6,9 @@
 //
 // As a matrix product: C = X . W^T with X int8 [M = batch * T, d_model] and
 // W int8 [N = 2 * heads * d, d_model] (row o = output feature o), on
-// v_mfma_i32_32x32x32_i8.  A workgroup of 4 waves owns a 128 x 128 tile of C
-// (each wave 64 x 64 = 2 x 2 MFMA tiles).  K is staged through two LDS
+// v_mfma_i32_32x32x32_i8.  A workgroup of 8 waves owns a 128 x 256 tile of C
+// (each wave 64 x 64 = 2 x 2 MFMA tiles), so a block of X rows is read by
+// half as many workgroups as with square tiles.  K is staged through two LDS
 // buffers 64 bytes at a time with 16-byte coalesced loads: the next stage's
 // global loads are in flight in registers while the current stage's MFMAs
 // run, so each stage costs one barrier and no exposed load latency.  The
@@ -23,8 +24,8 @@ namespace {
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kSplitThreads = 256;
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kSplitThreads = 512;
+constexpr int kBM = 128, kBN = 256, kBK = 64;
 constexpr int kInRow = kBK + 16;     // padded LDS row of a staged operand (bytes)
 constexpr int kOutRow = kBN + 16;    // padded LDS row of the int8 output tile
 
@@ -40,35 +41,37 @@ struct SplitLds {
     };
 };
 
-// This thread's two 16-byte chunks of X and of W for the stage at k0
-// (rows r = c / 4 for c = tid, tid + 256; chunk c % 4), zero outside.
+// This thread's 16-byte chunks of X (one) and of W (two) for the stage at
+// k0 (rows r = c / 4 for c = tid (+ 512 for W); chunk c % 4), zero outside.
 struct StageRegs {
-    int4 x[2], w[2];
+    int4 x[1], w[2];
 };
 
 __device__ __forceinline__ void load_stage(StageRegs& g, const int8_t* __restrict__ X,
                                            const int8_t* __restrict__ W, int m0, int n0, int k0,
                                            int M, int N, int dm, int tid)
 {
+    {
+        const int r = tid >> 2, kk = k0 + 16 * (tid & 3);
+        g.x[0] = make_int4(0, 0, 0, 0);
+        if (m0 + r < M && kk < dm) g.x[0] = *reinterpret_cast<const int4*>(X + (size_t)(m0 + r) * dm + kk);
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int c = tid + i * kSplitThreads;
         const int r = c >> 2, kk = k0 + 16 * (c & 3);
-        g.x[i] = make_int4(0, 0, 0, 0);
         g.w[i] = make_int4(0, 0, 0, 0);
-        if (m0 + r < M && kk < dm) g.x[i] = *reinterpret_cast<const int4*>(X + (size_t)(m0 + r) * dm + kk);
         if (n0 + r < N && kk < dm) g.w[i] = *reinterpret_cast<const int4*>(W + (size_t)(n0 + r) * dm + kk);
     }
 }
 
 __device__ __forceinline__ void store_stage(SplitStage& st, const StageRegs& g, int tid)
 {
+    *reinterpret_cast<int4*>(st.x + (tid >> 2) * kInRow + 16 * (tid & 3)) = g.x[0];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int c = tid + i * kSplitThreads;
-        const int off = (c >> 2) * kInRow + 16 * (c & 3);
-        *reinterpret_cast<int4*>(st.x + off) = g.x[i];
-        *reinterpret_cast<int4*>(st.w + off) = g.w[i];
+        *reinterpret_cast<int4*>(st.w + (c >> 2) * kInRow + 16 * (c & 3)) = g.w[i];
     }
 }
 
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(4
     if (lb >= nbm * nbn) return;   // grid padding, uniform over the workgroup
     const int bm = lb / nbn, bn = lb % nbn;
     const int m0 = bm * kBM, n0 = bn * kBN;
-    const int wm = (wv >> 1) * 64, wn = (wv & 1) * 64;        // this wave's 64 x 64 sub-tile
+    const int wm = (wv >> 2) * 64, wn = (wv & 3) * 64;        // this wave's 64 x 64 sub-tile
     const int col = lane & 31, half = lane >> 5;
     const int stages = (dm + kBK - 1) / kBK;
 
