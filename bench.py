@@ -6,8 +6,8 @@
 A step is one pass of the whole prefill path over one batch: tree build and
 budget prediction (alhr_prepare: the two share their launches), then the
 fused route + attend kernel, i.e. the kernels alhr_forward launches, issued
-as its two ABI calls back to back, with HIP events on the launch stream
-around each call.  Untimed auxiliary measurements (the
+as its two ABI calls back to back, with fence-free HIP timing events on the
+launch stream around the route call.  Untimed auxiliary measurements (the
 routing's load counts, the dense baseline, the splitter) run first.  Inputs
 are synthetic and resident in HBM before the timed region.  Prints one JSON
 line:
@@ -299,6 +299,57 @@ def step_calls(alhr, cfg, q, k, v, wt, nodes, budget, ws, fixed, idx, count, O):
                            count, O)
 
 
+class TimingEvents:
+    """n HIP timing events created with hipEventDisableSystemFence, recorded
+    on torch's current stream (the stream the binding launches on).
+
+    A default event ends with a system-scope release: when it completes, the
+    GPU writes back and invalidates its caches, so the kernel launched after
+    it starts later (about 5 us per event here) and on a cold L2.  These
+    events only timestamp the stream; the host reads them after a device
+    synchronisation, so they need no fence.  The HIP runtime is the one torch
+    has already loaded (same soname), so the stream handles are shared."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, torch, n):
+        import ctypes
+        self._c = ctypes
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip = hip
+        self._stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self._ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            self._check(hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE),
+                        "hipEventCreateWithFlags")
+            self._ev.append(e)
+
+    @staticmethod
+    def _check(rc, what):
+        if rc != 0:
+            raise RuntimeError("%s failed with HIP error %d" % (what, rc))
+
+    def record(self, i):
+        self._check(self._hip.hipEventRecord(self._ev[i], self._stream), "hipEventRecord")
+
+    def ms(self, a, b):
+        f = self._c.c_float()
+        self._check(self._hip.hipEventElapsedTime(self._c.byref(f), self._ev[a], self._ev[b]),
+                    "hipEventElapsedTime")
+        return f.value
+
+    def close(self):
+        for e in self._ev:
+            self._hip.hipEventDestroy(e)
+        self._ev = []
+
+
 def capture_step(torch, fn):
     """fn's launches captured in a HIP graph (on torch's capture stream, which
     the binding launches on)."""
@@ -406,13 +457,16 @@ def bench_prefill(args, torch, dev):
 
     # The timed steps: each one is the two calls, the preparation (tree +
     # budgets, alhr_prepare) and the fused route + attend (alhr_route_attend),
-    # launched directly, with HIP events on the launch stream (torch's current
-    # stream, on which the binding launches) before, between and after them,
-    # so the route kernel's duration is measured in the timed region itself.
+    # launched directly, with a fence-free HIP timing event on the launch
+    # stream before and after the route call, so the route kernel's duration
+    # is measured in the timed region itself; the span from one route call's
+    # end to the next one's start is the preparation with its launch gaps.
     # A step takes about half a millisecond of GPU time and its three launches
     # a few tens of microseconds of host time, so the host stays ahead and the
     # kernels run back to back (replaying each call as a HIP graph instead
-    # added about 8 microseconds per graph on this platform).
+    # added about 8 microseconds per graph on this platform; torch's default
+    # events, three per step, added about 10 microseconds per step through
+    # their cache write-back and invalidation).
     def prep():
         alhr.alhr_prepare(cfg, q, k, wb, nodes, bb, wsb)
 
@@ -425,20 +479,22 @@ def bench_prefill(args, torch, dev):
     for _ in range(SETTLE_STEPS + args.warmup):
         prep()
         route()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-              for _ in range(args.steps)]
+    events = TimingEvents(torch, 2 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e in events:
-        e[0].record()
+    for i in range(args.steps):
         prep()
-        e[1].record()
+        events.record(2 * i)
         route()
-        e[2].record()
+        events.record(2 * i + 1)
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    kern = {name: float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
-            for name, a, b in (("prepare_ms", 0, 1), ("route_attend_ms", 1, 2))}
+    kern = {"route_attend_ms": float(np.mean([events.ms(2 * i, 2 * i + 1)
+                                              for i in range(args.steps)])),
+            "prepare_and_gaps_ms": (float(np.mean([events.ms(2 * i - 1, 2 * i)
+                                                   for i in range(1, args.steps)]))
+                                    if args.steps > 1 else None)}
+    events.close()
 
     bpl = int(bytes_per_query(stats, cfg, wt is not None).sum())
     counted = args.workload == "t16k" and not args.budget_override
@@ -702,20 +758,23 @@ def bench_sweep(args, torch, dev):
         O = torch.empty(shape, dtype=torch.float32, device=dev)
         ws = torch.empty(max(alhr.alhr_workspace_bytes(cfg), 256), dtype=torch.uint8, device=dev)
 
-        def step(ev):
-            ev[0].record()
+        evs = TimingEvents(torch, 2 * args.steps)
+
+        def step(i):
             alhr.alhr_prepare(cfg, Q, K, Wt, nodes, bud, ws)
-            ev[1].record()
+            if i is not None:
+                evs.record(2 * i)
             alhr.alhr_route_attend(cfg, Q, K, V, nodes, bud, 0, idx, cnt, O)
-            ev[2].record()
+            if i is not None:
+                evs.record(2 * i + 1)
         for _ in range(2):
-            step([torch.cuda.Event(enable_timing=True) for _ in range(3)])
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+            step(None)
         torch.cuda.synchronize()
-        for e in evs:
-            step(e)
+        for i in range(args.steps):
+            step(i)
         torch.cuda.synchronize()
-        kms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        kms = float(np.mean([evs.ms(2 * i, 2 * i + 1) for i in range(args.steps)]))
+        evs.close()
         # step time from graph replays of the same calls (at the short lengths
         # a step takes about as long as the host needs to issue its launches)
         graph = capture_step(torch, lambda: step_calls(alhr, cfg, Q, K, V, Wt, nodes, bud, ws, 0,
