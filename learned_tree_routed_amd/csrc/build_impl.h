@@ -86,13 +86,30 @@ __device__ __forceinline__ void build_tile(int blk, int4* lvl, const void* __res
     {
         const size_t out_row0 = (size_t)(T >> out_level) + in_first / 2;
         const bool narrow = out_level <= l16;
-        for (int c = threadIdx.x; c < rows * C4; c += kBuildThreads) {
+        // every load of the level issued before the first sum (a tile's
+        // first level is at most kTileElems / 8 chunks, kFirstPer per thread);
+        // the loads are unconditional, chunks past the level re-reading its
+        // last chunk, so that nothing separates them
+        constexpr int kFirstPer = kTileElems / 2 / 4 / kBuildThreads;
+        const int last = rows * C4 - 1;
+        int4 a[kFirstPer], b[kFirstPer];
+#pragma unroll
+        for (int u = 0; u < kFirstPer; ++u) {
+            const int c = min(threadIdx.x + u * kBuildThreads, last);
             const int j = c / C4, g = c % C4;
-            const int4 a = load_chunk<D, IN>(in_pair, T, l16, in_row0 + 2 * j, g);
-            const int4 b = load_chunk<D, IN>(in_pair, T, l16, in_row0 + 2 * j + 1, g);
-            const int4 sum = make_int4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
-            lvl[c] = sum;
-            store_chunk<D>(out_pair, T, l16, out_row0 + j, g, sum, narrow);
+            a[u] = load_chunk<D, IN>(in_pair, T, l16, in_row0 + 2 * j, g);
+            b[u] = load_chunk<D, IN>(in_pair, T, l16, in_row0 + 2 * j + 1, g);
+        }
+#pragma unroll
+        for (int u = 0; u < kFirstPer; ++u) {
+            const int c = threadIdx.x + u * kBuildThreads;
+            if (c < rows * C4) {
+                const int j = c / C4, g = c % C4;
+                const int4 sum = make_int4(a[u].x + b[u].x, a[u].y + b[u].y, a[u].z + b[u].z,
+                                           a[u].w + b[u].w);
+                lvl[c] = sum;
+                store_chunk<D>(out_pair, T, l16, out_row0 + j, g, sum, narrow);
+            }
         }
     }
     // later levels from the LDS copy of the level below

@@ -121,15 +121,23 @@ __device__ __forceinline__ void predict_chunks_block(int blk, ChunksLds<D>& sm,
     const int pair = blk / nch, chunk = blk % nch;
     const int g = threadIdx.x % C4, rg = threadIdx.x / C4;
     const int* kr = reinterpret_cast<const int*>(K) + (size_t)pair * T * C4;
+    // the thread's kChunk / RG = C4 rows, up to 16 loads in flight at a time
+    constexpr int NR = kChunk / RG, NB = NR < 16 ? NR : 16;
     int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
-    for (int r = rg; r < kChunk; r += RG) {
-        const int t = chunk * kChunk + r;
-        if (t < T) {
-            const int w = kr[(size_t)t * C4 + g];
-            a0 += sbyte(w, 0);
-            a1 += sbyte(w, 1);
-            a2 += sbyte(w, 2);
-            a3 += sbyte(w, 3);
+#pragma unroll
+    for (int r0 = 0; r0 < NR; r0 += NB) {
+        int w[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int t = chunk * kChunk + rg + (r0 + i) * RG;
+            w[i] = t < T ? kr[(size_t)t * C4 + g] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            a0 += sbyte(w[i], 0);
+            a1 += sbyte(w[i], 1);
+            a2 += sbyte(w[i], 2);
+            a3 += sbyte(w[i], 3);
         }
     }
     part[rg][4 * g + 0] = a0;
