@@ -145,6 +145,13 @@ __device__ __forceinline__ void dense_store(const DenseStage<D>& st, DenseTile<D
 // Every choice of the reference maximum gives the same softmax.
 constexpr float kMaxSlack = 8.0f;
 
+// 2^x by the hardware instruction alone (v_exp_f32, about 1 ulp): every
+// argument here is at most the slack above (the probabilities) or at most 0
+// (the rescaling factor, -inf on the first block giving 0), so the range
+// handling a general exp2f wraps around it is not needed; results below the
+// normal range are weights too small to move a sum that includes 1.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // One key block's product for the wave: S^T on the int8 matrix cores, the
 // online softmax update and O^T += V^T P^T.  MASK: the block holds keys past
 // a query of the wave (its diagonal) or past T.
@@ -176,7 +183,7 @@ __device__ __forceinline__ void dense_block(const DenseTile<D>& tl, int k0, int 
     const float mb = (float)smax * c1;
     const float mn = mb > m + kMaxSlack * 1.44269504f ? mb : m;
     if (__ballot(mn != m) != 0ull) {
-        const float corr = exp2f(m - mn);   // 1 where unchanged, 0 on the first block
+        const float corr = exp2_hw(m - mn);   // 1 where unchanged, 0 on the first block
         lsum *= corr;
 #pragma unroll
         for (int i = 0; i < NT; ++i) acc[i] *= corr;
@@ -186,7 +193,7 @@ __device__ __forceinline__ void dense_block(const DenseTile<D>& tl, int k0, int 
     float ps = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        p[r] = exp2f(__builtin_fmaf((float)sc[r], c1, -m));
+        p[r] = exp2_hw(__builtin_fmaf((float)sc[r], c1, -m));
         if (MASK) p[r] = ok[r] ? p[r] : 0.0f;
         ps += p[r];
     }
