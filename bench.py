@@ -311,6 +311,7 @@ class TimingEvents:
     has already loaded (same soname), so the stream handles are shared."""
 
     DISABLE_SYSTEM_FENCE = 0x20000000
+    kind = "HIP events without the system-scope fence"
 
     def __init__(self, torch, n):
         import ctypes
@@ -348,6 +349,37 @@ class TimingEvents:
         for e in self._ev:
             self._hip.hipEventDestroy(e)
         self._ev = []
+
+
+class TorchEvents:
+    """The same interface over torch's default timing events (with the
+    system-scope fence), used only when the fence-free events cannot be
+    created."""
+
+    kind = "torch default events"
+
+    def __init__(self, torch, n):
+        self._ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    def record(self, i):
+        self._ev[i].record()
+
+    def ms(self, a, b):
+        return self._ev[a].elapsed_time(self._ev[b])
+
+    def close(self):
+        self._ev = []
+
+
+def timing_events(torch, n):
+    """n fence-free HIP timing events, or torch's default events (reported
+    by their `kind`) when the HIP runtime refuses the flag."""
+    try:
+        return TimingEvents(torch, n)
+    except (OSError, AttributeError, RuntimeError) as e:
+        print("bench: fence-free HIP events unavailable (%s); using torch's events" % e,
+              file=sys.stderr)
+        return TorchEvents(torch, n)
 
 
 def capture_step(torch, fn):
@@ -479,7 +511,7 @@ def bench_prefill(args, torch, dev):
     for _ in range(SETTLE_STEPS + args.warmup):
         prep()
         route()
-    events = TimingEvents(torch, 2 * args.steps)
+    events = timing_events(torch, 2 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -493,7 +525,8 @@ def bench_prefill(args, torch, dev):
                                               for i in range(args.steps)])),
             "prepare_and_gaps_ms": (float(np.mean([events.ms(2 * i - 1, 2 * i)
                                                    for i in range(1, args.steps)]))
-                                    if args.steps > 1 else None)}
+                                    if args.steps > 1 else None),
+            "events": events.kind}
     events.close()
 
     bpl = int(bytes_per_query(stats, cfg, wt is not None).sum())
@@ -758,7 +791,7 @@ def bench_sweep(args, torch, dev):
         O = torch.empty(shape, dtype=torch.float32, device=dev)
         ws = torch.empty(max(alhr.alhr_workspace_bytes(cfg), 256), dtype=torch.uint8, device=dev)
 
-        evs = TimingEvents(torch, 2 * args.steps)
+        evs = timing_events(torch, 2 * args.steps)
 
         def step(i):
             alhr.alhr_prepare(cfg, Q, K, Wt, nodes, bud, ws)

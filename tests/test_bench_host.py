@@ -157,3 +157,31 @@ def test_committed_counter_summaries_match_the_source():
     assert bench.read_traffic() is not None
     assert bench.read_traffic(path=bench.PROFILE_DECODE_COUNTERS) is not None
     assert bench.read_issue(0.5, 131072) is not None
+
+
+def test_timing_events_fall_back_to_torch_events():
+    """Without a HIP device (or when the runtime refuses the fence-free flag)
+    the bench times with torch's events and says so."""
+    import types
+
+    class FakeEvent:
+        def __init__(self, enable_timing):
+            assert enable_timing
+
+        def record(self):
+            pass
+
+        def elapsed_time(self, other):
+            return 1.25
+
+    def no_stream():
+        raise RuntimeError("no device")
+
+    fake = types.SimpleNamespace(cuda=types.SimpleNamespace(Event=FakeEvent,
+                                                            current_stream=no_stream))
+    ev = bench.timing_events(fake, 2)
+    ev.record(0)
+    ev.record(1)
+    assert isinstance(ev, bench.TorchEvents) and ev.kind == "torch default events"
+    assert ev.ms(0, 1) == 1.25
+    ev.close()

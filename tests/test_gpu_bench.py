@@ -15,6 +15,7 @@ def test_fence_free_events_time_like_torch_events():
     b = a @ a
     torch.cuda.synchronize()
     ev = bench.TimingEvents(torch, 4)
+    assert ev.kind.startswith("HIP events")
     try:
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record()
