@@ -117,9 +117,9 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
 {
     return (uint32_t)wave_reduce_i((int)v, -1, [](int a, int b) { return (int)((uint32_t)a < (uint32_t)b ? a : b); });
 }
-__device__ __forceinline__ float wave_max_f(float v)
+__device__ __forceinline__ int wave_max_i32(int v)
 {
-    return wave_reduce_f(v, -INFINITY, [](float a, float b) { return a > b ? a : b; });
+    return wave_reduce_i(v, (int)0x80000000, [](int a, int b) { return a > b ? a : b; });
 }
 __device__ __forceinline__ float wave_sum_f(float v)
 {

@@ -368,8 +368,12 @@ __device__ int select_best_ns(const uint64_t* cand, int n, int r, uint64_t* beam
     uint32_t h[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
+        // every slot index is below kSlots, so the read needs no guard;
+        // slots past n are then cleared
         const int sl = lane + kWave * j;
-        k[j] = sl < n ? cand[sl] : 0ull;
+        const uint64_t v = cand[sl];
+        const uint32_t keep = (uint32_t)0 - (uint32_t)(sl < n);
+        k[j] = ((uint64_t)((uint32_t)(v >> 32) & keep) << 32) | ((uint32_t)v & keep);
         h[j] = (uint32_t)(k[j] >> 32);
     }
     int nvalid = 0;
@@ -586,6 +590,14 @@ __device__ __forceinline__ void write_scores(const WaveLds& sm, int C, int max_b
     for (int c = lane_id(); c < max_budget; c += kWave) score_row[c] = c < C ? sm.score[c] : 0;
 }
 
+// The attention logit fl32(score * scale), rounded on its own: never fused
+// with the subtraction of the maximum that follows it.
+__device__ __forceinline__ float logit(float score, float scale)
+{
+#pragma clang fp contract(off)
+    return score * scale;
+}
+
 // softmax over sm.score[0, C) * scale and the weighted sum of value rows,
 // returned per lane (see store_output).
 // Positions outside [0, T) (possible only in caller-supplied index sets,
@@ -599,11 +611,14 @@ __device__ float4 attend_selected(WaveLds& sm, int C, int T, float scale,
     const int lane = lane_id();
     const bool ok0 = lane < C && (!CHECK || (unsigned)sm.pos[lane] < (unsigned)T);
     const bool ok1 = lane + kWave < C && (!CHECK || (unsigned)sm.pos[lane + kWave] < (unsigned)T);
-    const float a0 = ok0 ? (float)sm.score[lane] * scale : -INFINITY;
-    const float a1 = ok1 ? (float)sm.score[lane + kWave] * scale : -INFINITY;
-    const float mx = wave_max_f(a0 > a1 ? a0 : a1);
-    const float e0 = ok0 ? __expf(a0 - mx) : 0.0f;
-    const float e1 = ok1 ? __expf(a1 - mx) : 0.0f;
+    // the largest logit is fl32(fl32(largest score) * scale): rounding to
+    // fp32 and multiplying by the positive scale are both monotone, so the
+    // maximum is taken on the integer scores (slots kMaxBudget = 2 * 64)
+    const int s0 = ok0 ? sm.score[lane] : (int)0x80000000;
+    const int s1 = ok1 ? sm.score[lane + kWave] : (int)0x80000000;
+    const float mx = logit((float)wave_max_i32(s0 > s1 ? s0 : s1), scale);
+    const float e0 = ok0 ? __expf(logit((float)s0, scale) - mx) : 0.0f;
+    const float e1 = ok1 ? __expf(logit((float)s1, scale) - mx) : 0.0f;
     if (lane < C) sm.w[lane] = e0;
     if (lane + kWave < C) sm.w[lane + kWave] = e1;
     const float z = wave_sum_f(e0 + e1);
@@ -1190,11 +1205,12 @@ __device__ void attend_block(BlockShared& bs, int C, int T, float scale,
     if (wv == 0) {
         const bool ok0 = lane < C && (unsigned)sm.pos[lane] < (unsigned)T;
         const bool ok1 = lane + kWave < C && (unsigned)sm.pos[lane + kWave] < (unsigned)T;
-        const float a0 = ok0 ? (float)sm.score[lane] * scale : -INFINITY;
-        const float a1 = ok1 ? (float)sm.score[lane + kWave] * scale : -INFINITY;
-        const float mx = wave_max_f(a0 > a1 ? a0 : a1);
-        const float e0 = ok0 ? __expf(a0 - mx) : 0.0f;
-        const float e1 = ok1 ? __expf(a1 - mx) : 0.0f;
+        // the maximum on the integer scores, as in attend_selected
+        const int s0 = ok0 ? sm.score[lane] : (int)0x80000000;
+        const int s1 = ok1 ? sm.score[lane + kWave] : (int)0x80000000;
+        const float mx = logit((float)wave_max_i32(s0 > s1 ? s0 : s1), scale);
+        const float e0 = ok0 ? __expf(logit((float)s0, scale) - mx) : 0.0f;
+        const float e1 = ok1 ? __expf(logit((float)s1, scale) - mx) : 0.0f;
         if (lane < C) sm.w[lane] = e0;
         if (lane + kWave < C) sm.w[lane + kWave] = e1;
         const float z = wave_sum_f(e0 + e1);
